@@ -1,0 +1,173 @@
+/*
+ * muon_step.h -- C ABI of the MI355X (gfx950) Muon optimizer step over flat buffers.
+ *
+ * What is computed (page "Add initial Muon+M-FSDPv2 implementation",
+ * Megatron-LM PR #6425, pseudocode block "Opt step", steps 1, 2, 4 and 6; and
+ * class FsdpMuon on the page
+ * "core.distributed.fsdp.src.megatron_fsdp.experimental.muon", methods
+ * _compute_momentum_inputs, _orthogonalize_updates, _apply_local_updates):
+ * for every 2-D matrix described by a muon_matrix_desc_t, with
+ * G = gradient, M = momentum, W = weights, all rows x cols row-major,
+ *
+ *   M  <- beta*M + G                              (state update, step 1)
+ *   U  <- G + beta*M   (Nesterov)   or   U <- M   (orthogonalization input, step 2)
+ *   O  <- s * NS(U),  s = sqrt(max(1, rows/cols)) (orthogonalization, step 4)
+ *   W  <- W*(1 - lr*wd) - lr*O                    (decoupled decay + update, step 6)
+ *
+ * NS is the quintic Newton-Schulz orthogonalization: X = U (or U^T when
+ * rows > cols), X <- X / (||X||_F + 1e-7), then ns_steps times
+ * A = X X^T, B = b A + c A A, X <- a X + B X with (a, b, c) =
+ * (3.4445, -4.7750, 2.0315); the result is transposed back for tall matrices.
+ * The pages name the orthogonalization without fixing its algorithm; the
+ * quintic iteration is the one Muon is built on.
+ *
+ * Numerics.  The elementwise phases run in float32, one rounding per
+ * operation, no fused multiply-add, in this order:
+ *   M1 = fl(fl(beta*M) + G);  U = fl(fl(beta*M1) + G)  (U = M1 without Nesterov)
+ *   f  = fl(1 - fl(lr*wd));   W1 = fl(W*f);  Wn = fl(W1 - fl(lr*O))
+ * and bfloat16 weights are rounded once, to nearest even, on store.
+ * The Frobenius norm is a deterministic float32 reduction.  Newton-Schulz
+ * runs either on bfloat16 MFMA with float32 accumulation and float32
+ * epilogues, X/A/B stored as bfloat16 (MUON_GEMM_BF16_MFMA), or entirely in
+ * float32 on the float32 MFMA (MUON_GEMM_F32).  O = fl(s * x) in float32.
+ * Results are deterministic and do not depend on the order of descriptors.
+ *
+ * Buffers.  All buffer pointers are device pointers allocated by the caller,
+ * who keeps ownership.  Descriptor arrays are host memory read during the
+ * call.  The workspace is caller-owned device memory of at least
+ * muon_workspace_bytes() bytes, 256-byte aligned; its contents are undefined
+ * after a call.  Calls that share a workspace must be ordered on one stream.
+ *
+ * Execution.  All work is enqueued on `stream` (0 = the null stream) and the
+ * call returns without waiting for it.  The first call with a new descriptor
+ * set (per device and GEMM mode) builds a launch plan and uploads its tables
+ * (one device allocation, kept until the process ends or the plan is evicted
+ * from a 32-entry cache); later calls with the same descriptors allocate
+ * nothing and do not synchronize the host.
+ *
+ * Errors.  Every entry point returns MUON_OK (0) or a negative muon_status_t.
+ * Every check except MUON_ERR_HIP runs before anything is enqueued, so a
+ * failed call leaves every buffer untouched.  muon_last_error() returns a
+ * thread-local message describing the last failure of this thread.  Values
+ * that are NaN or infinite inside the buffers are not checked: they propagate.
+ */
+#ifndef MUON_STEP_H
+#define MUON_STEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* One 2-D parameter inside the flat buffers (page "core.distributed.fsdp.src.
+ * megatron_fsdp.experimental.muon": FsdpMuon handles 2-D parameters only,
+ * held in flat FSDP buffers; the owner scatters slices of each full update to
+ * their shard destinations, "Opt step" step 5 of PR #6425).
+ *
+ *   offset        element offset of the row-major rows x cols matrix in the
+ *                 flat grads / momentum (and update) buffers; multiple of 4.
+ *   rows, cols    matrix shape, each >= 1.
+ *   param_offset  element offset of slice 0 in the flat params buffer.
+ *   shard_stride  distance in elements between consecutive slices in params
+ *                 (>= rows*cols/n_shards; ignored when n_shards == 1).
+ *   n_shards      the flattened matrix is cut into n_shards contiguous slices
+ *                 of rows*cols/n_shards elements; slice k of the update goes
+ *                 to params[param_offset + k*shard_stride ...].  For
+ *                 n_shards > 1 the slice length must be a multiple of 8.
+ *   reserved      must be 0.
+ * Every slice start must be 16-byte aligned within params.  Matrices must not
+ * overlap each other in grads/momentum, nor slices each other in params. */
+typedef struct muon_matrix_desc {
+    int64_t offset;
+    int64_t rows;
+    int64_t cols;
+    int64_t param_offset;
+    int64_t shard_stride;
+    int32_t n_shards;
+    int32_t reserved;
+} muon_matrix_desc_t;
+
+typedef enum muon_status {
+    MUON_OK = 0,
+    MUON_ERR_NULL_POINTER = -1,        /* a required pointer is NULL */
+    MUON_ERR_BAD_SHAPE = -2,           /* rows/cols < 1, numel % n_shards, slice length */
+    MUON_ERR_OUT_OF_BOUNDS = -3,       /* a matrix or slice leaves its buffer */
+    MUON_ERR_MISALIGNED = -4,          /* a matrix, slice or workspace start misaligned */
+    MUON_ERR_OVERLAP = -5,             /* two descriptors' ranges intersect */
+    MUON_ERR_ALIAS = -6,               /* two distinct buffers' address ranges intersect */
+    MUON_ERR_BAD_ARG = -7,             /* bad n, dtype, mode, ns_steps or non-finite scalar */
+    MUON_ERR_WORKSPACE_TOO_SMALL = -8, /* workspace smaller than muon_workspace_bytes() */
+    MUON_ERR_HIP = -9,                 /* a HIP runtime call failed (message has details) */
+    MUON_ERR_INTERNAL = -10            /* should not happen; message has details */
+} muon_status_t;
+
+/* Element type of the params buffer.  grads, momentum and updates are float32. */
+enum { MUON_DTYPE_F32 = 0, MUON_DTYPE_BF16 = 1 };
+
+/* Arithmetic of the Newton-Schulz chain. */
+enum { MUON_GEMM_BF16_MFMA = 0, MUON_GEMM_F32 = 1 };
+
+/* Bytes of device workspace that muon_step / muon_orthogonalize need for
+ * these descriptors and GEMM mode (the plan-building analogue of the owner
+ * assignment "computed during initialization" in FsdpMuon).  Host-only: makes
+ * no HIP call.  Validates the descriptors' shapes (not their bounds).
+ * out_bytes: host pointer receiving the size. */
+int muon_workspace_bytes(const muon_matrix_desc_t* descs, int64_t n, int gemm_mode,
+                         size_t* out_bytes);
+
+/* The whole step ("Opt step" steps 1, 2, 4, 6 of PR #6425; FsdpMuon.step).
+ *   params        device, n_param_elems elements of param_dtype; updated in place.
+ *   grads         device, float32, n_state_elems elements; read only.
+ *   momentum      device, float32, n_state_elems elements; updated in place.
+ *   descs, n      host array of n descriptors (n == 0 is a no-op).
+ *   lr, weight_decay, beta  finite float32 scalars.
+ *   nesterov      0 or 1.   ns_steps  0..64.   gemm_mode  MUON_GEMM_*.
+ *   workspace     device, >= muon_workspace_bytes(), 256-byte aligned.
+ * The four buffers must not alias one another. */
+int muon_step(void* params, int param_dtype, int64_t n_param_elems, const float* grads,
+              float* momentum, int64_t n_state_elems, const muon_matrix_desc_t* descs,
+              int64_t n, float lr, float weight_decay, float beta, int nesterov, int ns_steps,
+              int gemm_mode, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Momentum update and orthogonalization input alone ("Opt step" steps 1-2;
+ * FsdpMuon._compute_momentum_inputs).  Writes U (float32) to u_out at each
+ * descriptor's offset; momentum updated in place.  grads, momentum, u_out are
+ * device buffers of n_state_elems float32 that must not alias.  Weight decay
+ * is applied by muon_apply (decoupled), not here. */
+int muon_momentum(const float* grads, float* momentum, float* u_out, int64_t n_state_elems,
+                  const muon_matrix_desc_t* descs, int64_t n, float beta, int nesterov,
+                  hipStream_t stream);
+
+/* Orthogonalization alone ("Opt step" step 4; FsdpMuon._orthogonalize_updates):
+ * o_out = s * NS(u) for every descriptor, both device float32 buffers of
+ * n_elems elements laid out like grads.  o_out may equal u (in place) but must
+ * not partially overlap it.  Workspace as for muon_step. */
+int muon_orthogonalize(const float* u, float* o_out, int64_t n_elems,
+                       const muon_matrix_desc_t* descs, int64_t n, int ns_steps, int gemm_mode,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Decay and update alone ("Opt step" step 6; FsdpMuon._apply_local_updates):
+ * params slice k <- fl(fl(W*f) - fl(lr*O)), f = fl(1 - fl(lr*weight_decay)),
+ * with O read from `updates` (device float32, n_update_elems, laid out like
+ * grads) and slices scattered as the descriptors say.  params and updates
+ * must not alias. */
+int muon_apply(void* params, int param_dtype, int64_t n_param_elems, const float* updates,
+               int64_t n_update_elems, const muon_matrix_desc_t* descs, int64_t n, float lr,
+               float weight_decay, hipStream_t stream);
+
+/* Static name of a status code ("MUON_OK", "MUON_ERR_BAD_SHAPE", ...). */
+const char* muon_status_string(int status);
+
+/* Message of the calling thread's last failure ("" if none); valid until the
+ * thread's next call into this library. */
+const char* muon_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_STEP_H */

@@ -1,0 +1,220 @@
+"""MI355X (gfx950) Muon optimizer step over flat buffers.
+
+A thin ctypes binding of ``libmuon_step.so`` (C ABI in ``include/muon_step.h``).
+It only marshals arguments: every step of the computation runs in the
+library's HIP kernels.  PyTorch provides device memory and the current
+stream.  If the library is missing, every entry point raises: there is no
+fallback.
+
+Entry points (same names as the C ABI):
+
+``muon_step``           momentum, Nesterov input, Newton-Schulz, decay + apply
+``muon_momentum``       momentum update and orthogonalization input only
+``muon_orthogonalize``  Newton-Schulz orthogonalization (with shape scale) only
+``muon_apply``          decoupled decay and update, scattered into slices
+``muon_workspace_bytes``
+
+Descriptors are objects with ``offset, rows, cols`` and optionally
+``param_offset`` (default ``offset``), ``shard_stride`` (0) and ``n_shards``
+(1), or tuples in that field order.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Iterable, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmuon_step.so")
+
+MUON_OK = 0
+MUON_DTYPE_F32 = 0
+MUON_DTYPE_BF16 = 1
+MUON_GEMM_BF16_MFMA = 0
+MUON_GEMM_F32 = 1
+_MODES = {"bf16": MUON_GEMM_BF16_MFMA, "f32": MUON_GEMM_F32}
+
+#: C names of every exported entry point (mirrors include/muon_step.h).
+EXPORTS = ("muon_workspace_bytes", "muon_step", "muon_momentum", "muon_orthogonalize",
+           "muon_apply", "muon_status_string", "muon_last_error")
+
+
+class MatrixDescC(ctypes.Structure):
+    """``muon_matrix_desc_t``."""
+
+    _fields_ = [("offset", ctypes.c_int64), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("param_offset", ctypes.c_int64), ("shard_stride", ctypes.c_int64),
+                ("n_shards", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class MuonError(RuntimeError):
+    """A non-zero status returned by the library."""
+
+    def __init__(self, status: int, name: str, message: str):
+        super().__init__(f"{name}: {message}")
+        self.status = status
+        self.name = name
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m newton_schulz_flat_amd.build` (no fallback exists)")
+    lib = ctypes.CDLL(path)
+    p, i64, i32, f32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float,
+                            ctypes.c_size_t)
+    dp = ctypes.POINTER(MatrixDescC)
+    lib.muon_workspace_bytes.argtypes = [dp, i64, i32, ctypes.POINTER(sz)]
+    lib.muon_step.argtypes = [p, i32, i64, p, p, i64, dp, i64, f32, f32, f32, i32, i32, i32, p,
+                              sz, p]
+    lib.muon_momentum.argtypes = [p, p, p, i64, dp, i64, f32, i32, p]
+    lib.muon_orthogonalize.argtypes = [p, p, i64, dp, i64, i32, i32, p, sz, p]
+    lib.muon_apply.argtypes = [p, i32, i64, p, i64, dp, i64, f32, f32, p]
+    lib.muon_status_string.argtypes = [i32]
+    lib.muon_status_string.restype = ctypes.c_char_p
+    lib.muon_last_error.argtypes = []
+    lib.muon_last_error.restype = ctypes.c_char_p
+    for name in ("muon_workspace_bytes", "muon_step", "muon_momentum", "muon_orthogonalize",
+                 "muon_apply"):
+        getattr(lib, name).restype = i32
+    _lib = lib
+    return lib
+
+
+def check(status: int) -> None:
+    """Raise MuonError for a non-zero status."""
+    if status != MUON_OK:
+        lib = load_library()
+        raise MuonError(status, lib.muon_status_string(status).decode(),
+                        lib.muon_last_error().decode())
+
+
+def descs_array(descs: Iterable) -> ctypes.Array:
+    """Descriptors as a ``muon_matrix_desc_t`` array."""
+    items = list(descs)
+    arr = (MatrixDescC * max(1, len(items)))()
+    for k, d in enumerate(items):
+        if isinstance(d, (tuple, list)):
+            vals = list(d) + [None] * (6 - len(d))
+            off, rows, cols, poff, stride, shards = vals[:6]
+        else:
+            off, rows, cols = d.offset, d.rows, d.cols
+            poff = getattr(d, "param_offset", None)
+            stride = getattr(d, "shard_stride", None)
+            shards = getattr(d, "n_shards", None)
+        arr[k] = MatrixDescC(int(off), int(rows), int(cols), int(off if poff is None else poff),
+                             int(stride or 0), int(1 if shards is None else shards), 0)
+    return arr
+
+
+def _count(descs) -> int:
+    return len(descs) if isinstance(descs, Sequence) else len(list(descs))
+
+
+def _mode(mode: str) -> int:
+    try:
+        return _MODES[mode]
+    except KeyError:
+        raise ValueError(f"mode must be one of {sorted(_MODES)}, got {mode!r}") from None
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _require(t, name, dtypes):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def muon_workspace_bytes(descs, mode: str = "bf16") -> int:
+    lib = load_library()
+    arr = descs_array(descs)
+    out = ctypes.c_size_t(0)
+    check(lib.muon_workspace_bytes(arr, _count(descs), _mode(mode), ctypes.byref(out)))
+    return out.value
+
+
+_workspaces: dict = {}
+
+
+def workspace_for(descs, mode: str, device):
+    """A cached uint8 workspace tensor of at least the needed size on ``device``."""
+    import torch
+    need = muon_workspace_bytes(descs, mode)
+    key = torch.device(device)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=key)
+        _workspaces[key] = ws
+    return ws
+
+
+def muon_step(params, grads, momentum, descs, lr: float, weight_decay: float, beta: float,
+              nesterov: bool = True, ns_steps: int = 5, mode: str = "bf16", workspace=None):
+    """One Muon step in place on ``params`` (f32 or bf16) and ``momentum`` (f32)."""
+    import torch
+    _require(params, "params", (torch.float32, torch.bfloat16))
+    _require(grads, "grads", (torch.float32,))
+    _require(momentum, "momentum", (torch.float32,))
+    if workspace is None:
+        workspace = workspace_for(descs, mode, grads.device)
+    lib = load_library()
+    dt = MUON_DTYPE_BF16 if params.dtype == torch.bfloat16 else MUON_DTYPE_F32
+    check(lib.muon_step(params.data_ptr(), dt, params.numel(), grads.data_ptr(),
+                        momentum.data_ptr(), grads.numel(), descs_array(descs), _count(descs),
+                        lr, weight_decay, beta, int(bool(nesterov)), int(ns_steps), _mode(mode),
+                        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                        _stream(grads)))
+
+
+def muon_momentum(grads, momentum, u_out, descs, beta: float, nesterov: bool = True):
+    """Momentum update (in place) and orthogonalization input written to ``u_out``."""
+    import torch
+    for t, nm in ((grads, "grads"), (momentum, "momentum"), (u_out, "u_out")):
+        _require(t, nm, (torch.float32,))
+    lib = load_library()
+    check(lib.muon_momentum(grads.data_ptr(), momentum.data_ptr(), u_out.data_ptr(),
+                            grads.numel(), descs_array(descs), _count(descs), beta,
+                            int(bool(nesterov)), _stream(grads)))
+
+
+def muon_orthogonalize(u, o_out, descs, ns_steps: int = 5, mode: str = "bf16", workspace=None):
+    """``o_out = sqrt(max(1, rows/cols)) * NS(u)`` for every descriptor."""
+    import torch
+    _require(u, "u", (torch.float32,))
+    _require(o_out, "o_out", (torch.float32,))
+    if workspace is None:
+        workspace = workspace_for(descs, mode, u.device)
+    lib = load_library()
+    check(lib.muon_orthogonalize(u.data_ptr(), o_out.data_ptr(), u.numel(), descs_array(descs),
+                                 _count(descs), int(ns_steps), _mode(mode), workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), _stream(u)))
+
+
+def muon_apply(params, updates, descs, lr: float, weight_decay: float):
+    """``W <- W (1 - lr wd) - lr O`` scattered into ``params`` slices."""
+    import torch
+    _require(params, "params", (torch.float32, torch.bfloat16))
+    _require(updates, "updates", (torch.float32,))
+    lib = load_library()
+    dt = MUON_DTYPE_BF16 if params.dtype == torch.bfloat16 else MUON_DTYPE_F32
+    check(lib.muon_apply(params.data_ptr(), dt, params.numel(), updates.data_ptr(),
+                         updates.numel(), descs_array(descs), _count(descs), lr, weight_decay,
+                         _stream(updates)))

@@ -1,0 +1,36 @@
+// Device helpers shared by the gfx950 kernels of the Muon step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "muon_internal.h"
+
+namespace muon {
+
+// Matrix owning workgroup b: the largest m with prefix[m] <= b.  prefix has
+// n + 1 non-decreasing entries and every matrix owns at least one workgroup.
+__device__ __forceinline__ int owner_of(const int32_t* __restrict__ prefix, int n, int b) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (prefix[mid] <= b)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// float32 -> bfloat16 bits, round to nearest even (IEEE-754 definition on the
+// bit pattern); NaN becomes a quiet NaN keeping sign and top payload bits.
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+    const uint32_t b = __float_as_uint(x);
+    if ((b & 0x7fffffffu) > 0x7f800000u) return uint16_t((b >> 16) | 0x40u);
+    const uint32_t lsb = (b >> 16) & 1u;
+    return uint16_t((b + 0x7fffu + lsb) >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+}  // namespace muon

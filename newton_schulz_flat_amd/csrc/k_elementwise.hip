@@ -1,0 +1,192 @@
+// Elementwise phases of the Muon step on gfx950: momentum update and
+// orthogonalization input ("Opt step" steps 1-2 of PR #6425,
+// FsdpMuon._compute_momentum_inputs), the per-chunk sum of squares feeding
+// the Frobenius norm, and the decoupled decay + update with the scatter of
+// update slices to their shard destinations ("Opt step" steps 5-6,
+// FsdpMuon._apply_local_updates).
+//
+// All three are HBM-bound streams: each workgroup owns one chunk of
+// 256 x 4 x 8 consecutive elements of one matrix and moves them with 16-byte
+// (float4) loads and stores, consecutive lanes on consecutive vectors.
+// Floating-point contraction is off so that every multiply and add rounds on
+// its own, in the documented order (bit-exact against a same-order float32
+// reference).
+#include "k_common.h"
+
+#pragma clang fp contract(off)
+
+namespace muon {
+
+namespace {
+
+// Deterministic block sum of one float per thread (fixed shuffle tree, then
+// the 4 wave sums in order).
+__device__ __forceinline__ float block_sum(float v, float* lds4) {
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (lane == 0) lds4[wave] = v;
+    __syncthreads();
+    float t = 0.f;
+    if (threadIdx.x == 0) t = ((lds4[0] + lds4[1]) + lds4[2]) + lds4[3];
+    return t;
+}
+
+// kMode 0: M <- beta M + G, U <- G + beta M (or M); partial sums of U^2.
+// kMode 1: partial sums of U^2 only (U given).
+template <int kMode>
+__global__ __launch_bounds__(kEwThreads) void front_kernel(
+    const MatInfo* __restrict__ mats, const int32_t* __restrict__ prefix, int n,
+    const float* __restrict__ g, float* __restrict__ m, float* __restrict__ u,
+    float* __restrict__ partial, float beta, int nesterov) {
+    __shared__ float lds4[4];
+    const int blk = blockIdx.x;
+    const int mi = owner_of(prefix, n, blk);
+    const int64_t off = mats[mi].off;
+    const int64_t end = off + mats[mi].numel;
+    const int64_t base = off + int64_t(blk - mats[mi].chunk_begin) * kEwChunk;
+    float ss = 0.f;
+#pragma unroll
+    for (int it = 0; it < kEwIters; ++it) {
+        const int64_t e = base + (int64_t(it) * kEwThreads + threadIdx.x) * kEwVec;
+        if (e + kEwVec <= end) {
+            float4 uv;
+            if (kMode == 0) {
+                const float4 gv = *reinterpret_cast<const float4*>(g + e);
+                const float4 mv = *reinterpret_cast<const float4*>(m + e);
+                float4 m1;
+                m1.x = beta * mv.x + gv.x;
+                m1.y = beta * mv.y + gv.y;
+                m1.z = beta * mv.z + gv.z;
+                m1.w = beta * mv.w + gv.w;
+                *reinterpret_cast<float4*>(m + e) = m1;
+                if (nesterov) {
+                    uv.x = beta * m1.x + gv.x;
+                    uv.y = beta * m1.y + gv.y;
+                    uv.z = beta * m1.z + gv.z;
+                    uv.w = beta * m1.w + gv.w;
+                } else {
+                    uv = m1;
+                }
+                *reinterpret_cast<float4*>(u + e) = uv;
+            } else {
+                uv = *reinterpret_cast<const float4*>(u + e);
+            }
+            ss += uv.x * uv.x;
+            ss += uv.y * uv.y;
+            ss += uv.z * uv.z;
+            ss += uv.w * uv.w;
+        } else {
+            for (int64_t k = e; k < end && k < e + kEwVec; ++k) {
+                float uk;
+                if (kMode == 0) {
+                    const float gk = g[k];
+                    const float m1 = beta * m[k] + gk;
+                    m[k] = m1;
+                    uk = nesterov ? beta * m1 + gk : m1;
+                    u[k] = uk;
+                } else {
+                    uk = u[k];
+                }
+                ss += uk * uk;
+            }
+        }
+    }
+    if (partial != nullptr) {
+        const float t = block_sum(ss, lds4);
+        if (threadIdx.x == 0) partial[blk] = t;
+    }
+}
+
+__device__ __forceinline__ void store_w(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+__device__ __forceinline__ void store_w(uint16_t* p, float4 v) {
+    const uint32_t lo = uint32_t(bf16_rne(v.x)) | (uint32_t(bf16_rne(v.y)) << 16);
+    const uint32_t hi = uint32_t(bf16_rne(v.z)) | (uint32_t(bf16_rne(v.w)) << 16);
+    *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+}
+__device__ __forceinline__ float4 load_w(const float* p) {
+    return *reinterpret_cast<const float4*>(p);
+}
+__device__ __forceinline__ float4 load_w(const uint16_t* p) {
+    const uint2 b = *reinterpret_cast<const uint2*>(p);
+    return make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xffff0000u),
+                       __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xffff0000u));
+}
+__device__ __forceinline__ float load_w1(const float* p) { return *p; }
+__device__ __forceinline__ float load_w1(const uint16_t* p) { return bf16_to_f32(*p); }
+__device__ __forceinline__ void store_w1(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_w1(uint16_t* p, float v) { *p = bf16_rne(v); }
+
+// W1 = fl(W f); Wn = fl(W1 - fl(lr O)); element j of the flattened matrix
+// lives in slice j / slice_len at param offset poff + k pstride + j % slice_len.
+template <typename TW>
+__global__ __launch_bounds__(kEwThreads) void apply_kernel(
+    const MatInfo* __restrict__ mats, const int32_t* __restrict__ prefix, int n,
+    TW* __restrict__ w, const float* __restrict__ o, float decay, float lr) {
+    const int blk = blockIdx.x;
+    const int mi = owner_of(prefix, n, blk);
+    const MatInfo& mt = mats[mi];
+    const int64_t numel = mt.numel, off = mt.off, poff = mt.poff;
+    const int64_t slice = mt.slice_len, stride = mt.pstride;
+    const bool sharded = slice != numel;
+    const int64_t base = int64_t(blk - mt.chunk_begin) * kEwChunk;
+#pragma unroll
+    for (int it = 0; it < kEwIters; ++it) {
+        const int64_t j = base + (int64_t(it) * kEwThreads + threadIdx.x) * kEwVec;
+        if (j + kEwVec <= numel) {
+            // slices are multiples of 8 long when sharded: a vector never straddles two
+            int64_t dst = poff + j;
+            if (sharded) {
+                const int64_t k = j / slice;
+                dst = poff + k * stride + (j - k * slice);
+            }
+            const float4 ov = *reinterpret_cast<const float4*>(o + off + j);
+            const float4 wv = load_w(w + dst);
+            float4 r;
+            r.x = wv.x * decay - lr * ov.x;
+            r.y = wv.y * decay - lr * ov.y;
+            r.z = wv.z * decay - lr * ov.z;
+            r.w = wv.w * decay - lr * ov.w;
+            store_w(w + dst, r);
+        } else {
+            for (int64_t k = j; k < numel && k < j + kEwVec; ++k) {
+                const int64_t s = sharded ? k / slice : 0;
+                const int64_t dst = poff + s * stride + (k - s * slice);
+                const float w1 = load_w1(w + dst) * decay;
+                const float t = lr * o[off + k];
+                store_w1(w + dst, w1 - t);
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_front(const PlanView& p, const float* grads, float* momentum, float* u,
+                        float* partial, float beta, int nesterov, hipStream_t s) {
+    if (p.total_chunks == 0) return hipSuccess;
+    front_kernel<0><<<dim3(unsigned(p.total_chunks)), dim3(kEwThreads), 0, s>>>(
+        p.mats, p.chunk_prefix, p.n, grads, momentum, u, partial, beta, nesterov);
+    return hipGetLastError();
+}
+
+hipError_t launch_sumsq(const PlanView& p, const float* u, float* partial, hipStream_t s) {
+    if (p.total_chunks == 0) return hipSuccess;
+    front_kernel<1><<<dim3(unsigned(p.total_chunks)), dim3(kEwThreads), 0, s>>>(
+        p.mats, p.chunk_prefix, p.n, nullptr, nullptr, const_cast<float*>(u), partial, 0.f, 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_apply(const PlanView& p, void* params, int param_dtype, const float* o,
+                        float decay, float lr, hipStream_t s) {
+    if (p.total_chunks == 0) return hipSuccess;
+    const dim3 grid{static_cast<unsigned>(p.total_chunks)}, block{kEwThreads};
+    if (param_dtype == MUON_DTYPE_BF16)
+        apply_kernel<uint16_t><<<grid, block, 0, s>>>(p.mats, p.chunk_prefix, p.n,
+                                                      static_cast<uint16_t*>(params), o, decay, lr);
+    else
+        apply_kernel<float><<<grid, block, 0, s>>>(p.mats, p.chunk_prefix, p.n,
+                                                   static_cast<float*>(params), o, decay, lr);
+    return hipGetLastError();
+}
+
+}  // namespace muon

@@ -1,0 +1,130 @@
+// Frobenius normalization and layout change into the Newton-Schulz
+// orientation, on gfx950.
+//
+// norm_kernel: one workgroup per matrix sums that matrix's per-chunk partial
+// sums of squares in a fixed order and stores inv = 1 / (sqrt(sum) + 1e-7).
+//
+// cast_kernel: one workgroup per 64 x 64 tile of the padded NS-orientation
+// matrix (rp x cp).  It reads the matching 64 x 64 block of U in U's own
+// row-major orientation (coalesced along U's rows), scales it by inv, and
+// writes both X0 (rp x cp) and X0^T (cp x rp) -- the two layouts the GEMM
+// stages read -- through an LDS transpose, so every global access runs along
+// a row.  Tall matrices (rows > cols) are transposed into the wide
+// orientation here.  Elements outside the r x c matrix are written as zero,
+// which the Newton-Schulz products preserve.  With ns_steps == 0 it writes
+// O = fl(s * X0) in U's own layout instead.
+#include "k_common.h"
+
+#pragma clang fp contract(off)
+
+namespace muon {
+
+namespace {
+
+constexpr int kNormThreads = 256;
+
+__global__ __launch_bounds__(kNormThreads) void norm_kernel(const MatInfo* __restrict__ mats,
+                                                            const float* __restrict__ partial,
+                                                            float* __restrict__ inv) {
+    __shared__ float red[kNormThreads];
+    const int mi = blockIdx.x;
+    const int begin = mats[mi].chunk_begin, count = mats[mi].n_chunks;
+    float s = 0.f;
+    for (int i = threadIdx.x; i < count; i += kNormThreads) s += partial[begin + i];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = kNormThreads / 2; w >= 1; w >>= 1) {
+        if (threadIdx.x < w) red[threadIdx.x] = red[threadIdx.x] + red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) inv[mi] = 1.0f / (sqrtf(red[0]) + kNormEps);
+}
+
+__device__ __forceinline__ void store_x(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_x(uint16_t* p, float v) { *p = bf16_rne(v); }
+__device__ __forceinline__ float rounded(float v, float*) { return v; }
+__device__ __forceinline__ float rounded(float v, uint16_t*) { return bf16_to_f32(bf16_rne(v)); }
+
+template <typename TX>
+__global__ __launch_bounds__(256) void cast_kernel(const MatInfo* __restrict__ mats,
+                                                   const int32_t* __restrict__ prefix, int n,
+                                                   const float* u,  // may equal o_direct
+                                                   const float* __restrict__ inv,
+                                                   TX* __restrict__ x, TX* __restrict__ xt,
+                                                   float* o_direct) {
+    constexpr int T = kCastTile;
+    __shared__ float tile[T][T + 1];
+    const int blk = blockIdx.x;
+    const int mi = owner_of(prefix, n, blk);
+    const MatInfo& mt = mats[mi];
+    const int t = blk - mt.cast_begin;
+    const int ntj = mt.cp / T;
+    const int ti = t / ntj, tj = t % ntj;
+    const bool tall = mt.tall != 0;
+    // Tile origin in U's own (R x C) coordinates.
+    const int ur0 = tall ? tj * T : ti * T;
+    const int uc0 = tall ? ti * T : tj * T;
+    const float scale_inv = inv[mi];
+    const float* um = u + mt.off;
+    for (int idx = threadIdx.x; idx < T * T; idx += 256) {
+        const int rr = idx / T, cc = idx % T;
+        const int gr = ur0 + rr, gc = uc0 + cc;
+        float v = 0.f;
+        if (gr < mt.R && gc < mt.C) v = um[int64_t(gr) * mt.C + gc] * scale_inv;
+        tile[rr][cc] = v;
+    }
+    __syncthreads();
+    if (o_direct != nullptr) {
+        // No iterations: O = fl(s * X0), X0 rounded to the storage type.
+        float* om = o_direct + mt.off;
+        for (int idx = threadIdx.x; idx < T * T; idx += 256) {
+            const int rr = idx / T, cc = idx % T;
+            const int gr = ur0 + rr, gc = uc0 + cc;
+            if (gr < mt.R && gc < mt.C)
+                om[int64_t(gr) * mt.C + gc] = mt.scale * rounded(tile[rr][cc], x);
+        }
+        return;
+    }
+    TX* xm = x + mt.x_off;
+    TX* xtm = xt + mt.x_off;
+    // X0[i][j], i = ti*T + a, j = tj*T + b  (native element tile[a][b] or tile[b][a])
+    for (int idx = threadIdx.x; idx < T * T; idx += 256) {
+        const int a = idx / T, b = idx % T;
+        const float v = tall ? tile[b][a] : tile[a][b];
+        store_x(xm + int64_t(ti * T + a) * mt.cp + tj * T + b, v);
+    }
+    // X0^T[j][i], j = tj*T + a, i = ti*T + b
+    for (int idx = threadIdx.x; idx < T * T; idx += 256) {
+        const int a = idx / T, b = idx % T;
+        const float v = tall ? tile[a][b] : tile[b][a];
+        store_x(xtm + int64_t(tj * T + a) * mt.rp + ti * T + b, v);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_norm(const PlanView& p, const float* partial, float* inv, hipStream_t s) {
+    if (p.n == 0) return hipSuccess;
+    norm_kernel<<<dim3(unsigned(p.n)), dim3(kNormThreads), 0, s>>>(p.mats, partial, inv);
+    return hipGetLastError();
+}
+
+hipError_t launch_cast(const PlanView& p, const float* u, const float* inv, void* ws,
+                       float* o_direct, hipStream_t s) {
+    if (p.total_cast == 0) return hipSuccess;
+    unsigned char* w = static_cast<unsigned char*>(ws);
+    const dim3 grid{static_cast<unsigned>(p.total_cast)}, block{256};
+    if (p.gemm_mode == MUON_GEMM_F32)
+        cast_kernel<float><<<grid, block, 0, s>>>(p.mats, p.cast_prefix, p.n, u, inv,
+                                                  reinterpret_cast<float*>(w + p.ws.x),
+                                                  reinterpret_cast<float*>(w + p.ws.xt[0]),
+                                                  o_direct);
+    else
+        cast_kernel<uint16_t><<<grid, block, 0, s>>>(p.mats, p.cast_prefix, p.n, u, inv,
+                                                     reinterpret_cast<uint16_t*>(w + p.ws.x),
+                                                     reinterpret_cast<uint16_t*>(w + p.ws.xt[0]),
+                                                     o_direct);
+    return hipGetLastError();
+}
+
+}  // namespace muon

@@ -1,0 +1,266 @@
+// extern "C" entry points of the flat-buffer Muon step (declared, with their
+// contracts, in include/muon_step.h).  Each entry point validates everything
+// on the host first, then fetches the cached plan and enqueues its kernels on
+// the caller's stream.  Nothing is thrown across the ABI.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include <hip/hip_runtime.h>
+
+#include "muon_internal.h"
+
+using muon::Status;
+
+namespace {
+
+thread_local char t_last_error[512] = "";
+
+int finish(const Status& st) {
+    if (st.code != MUON_OK) {
+        std::strncpy(t_last_error, st.msg, sizeof(t_last_error) - 1);
+        t_last_error[sizeof(t_last_error) - 1] = '\0';
+    }
+    return st.code;
+}
+
+int hip_fail(Status* st, hipError_t e, const char* what) {
+    st->code = MUON_ERR_HIP;
+    snprintf(st->msg, sizeof(st->msg), "%s: %s", what, hipGetErrorString(e));
+    return st->code;
+}
+
+size_t param_bytes(int dtype, int64_t n) { return size_t(n) * (dtype == MUON_DTYPE_BF16 ? 2 : 4); }
+
+int check_mode(int gemm_mode, Status* st) {
+    if (gemm_mode != MUON_GEMM_BF16_MFMA && gemm_mode != MUON_GEMM_F32) {
+        st->code = MUON_ERR_BAD_ARG;
+        snprintf(st->msg, sizeof(st->msg), "gemm_mode %d is not MUON_GEMM_BF16_MFMA or _F32",
+                 gemm_mode);
+        return st->code;
+    }
+    return MUON_OK;
+}
+
+int check_ns_steps(int ns_steps, Status* st) {
+    if (ns_steps < 0 || ns_steps > muon::kMaxNsSteps) {
+        st->code = MUON_ERR_BAD_ARG;
+        snprintf(st->msg, sizeof(st->msg), "ns_steps %d is outside [0, %d]", ns_steps,
+                 muon::kMaxNsSteps);
+        return st->code;
+    }
+    return MUON_OK;
+}
+
+int check_flag(int v, const char* name, Status* st) {
+    if (v != 0 && v != 1) {
+        st->code = MUON_ERR_BAD_ARG;
+        snprintf(st->msg, sizeof(st->msg), "%s = %d must be 0 or 1", name, v);
+        return st->code;
+    }
+    return MUON_OK;
+}
+
+int check_null(const void* p, const char* name, Status* st) {
+    if (p == nullptr) {
+        st->code = MUON_ERR_NULL_POINTER;
+        snprintf(st->msg, sizeof(st->msg), "%s is NULL", name);
+        return st->code;
+    }
+    return MUON_OK;
+}
+
+int check_workspace(const void* ws, size_t have, size_t need, Status* st) {
+    if (need == 0) return MUON_OK;
+    if (ws == nullptr) return check_null(ws, "workspace", st);
+    if (reinterpret_cast<uintptr_t>(ws) % muon::kWsAlign != 0) {
+        st->code = MUON_ERR_MISALIGNED;
+        snprintf(st->msg, sizeof(st->msg), "workspace is not %zu-byte aligned", muon::kWsAlign);
+        return st->code;
+    }
+    if (have < need) {
+        st->code = MUON_ERR_WORKSPACE_TOO_SMALL;
+        snprintf(st->msg, sizeof(st->msg), "workspace has %zu bytes, needs %zu", have, need);
+        return st->code;
+    }
+    return MUON_OK;
+}
+
+#define TRY(expr)                                  \
+    do {                                           \
+        if ((expr) != MUON_OK) return finish(st);  \
+    } while (0)
+
+#define TRY_HIP(expr, what)                                      \
+    do {                                                         \
+        hipError_t e_ = (expr);                                  \
+        if (e_ != hipSuccess) return finish((hip_fail(&st, e_, what), st)); \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int muon_workspace_bytes(const muon_matrix_desc_t* descs, int64_t n, int gemm_mode,
+                         size_t* out_bytes) {
+    Status st{MUON_OK, ""};
+    TRY(check_null(out_bytes, "out_bytes", &st));
+    TRY(check_mode(gemm_mode, &st));
+    TRY(muon::check_desc_shapes(descs, n, &st));
+    *out_bytes = muon::workspace_bytes_for(descs, n, gemm_mode);
+    return MUON_OK;
+}
+
+int muon_step(void* params, int param_dtype, int64_t n_param_elems, const float* grads,
+              float* momentum, int64_t n_state_elems, const muon_matrix_desc_t* descs, int64_t n,
+              float lr, float weight_decay, float beta, int nesterov, int ns_steps, int gemm_mode,
+              void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    Status st{MUON_OK, ""};
+    TRY(muon::check_desc_shapes(descs, n, &st));
+    TRY(check_mode(gemm_mode, &st));
+    TRY(check_ns_steps(ns_steps, &st));
+    TRY(check_flag(nesterov, "nesterov", &st));
+    TRY(muon::check_scalar(lr, "lr", &st));
+    TRY(muon::check_scalar(weight_decay, "weight_decay", &st));
+    TRY(muon::check_scalar(beta, "beta", &st));
+    if (param_dtype != MUON_DTYPE_F32 && param_dtype != MUON_DTYPE_BF16)
+        TRY(muon::check_param_ranges(descs, 0, 0, param_dtype, &st));
+    if (n == 0) return MUON_OK;
+    TRY(check_null(params, "params", &st));
+    TRY(check_null(grads, "grads", &st));
+    TRY(check_null(momentum, "momentum", &st));
+    TRY(muon::check_state_ranges(descs, n, n_state_elems, "grads/momentum", &st));
+    TRY(muon::check_param_ranges(descs, n, n_param_elems, param_dtype, &st));
+    const size_t need = muon::workspace_bytes_for(descs, n, gemm_mode);
+    TRY(check_workspace(workspace, workspace_bytes, need, &st));
+    const muon::Range ranges[4] = {
+        {params, param_bytes(param_dtype, n_param_elems), "params"},
+        {grads, size_t(n_state_elems) * 4, "grads"},
+        {momentum, size_t(n_state_elems) * 4, "momentum"},
+        {workspace, workspace_bytes, "workspace"}};
+    TRY(muon::check_no_alias(ranges, 4, &st));
+
+    std::shared_ptr<const muon::PlanStore> plan;
+    TRY(muon::get_plan(descs, n, gemm_mode, stream, &plan, &st));
+    const muon::PlanView& p = muon::view_of(*plan);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    float* u = reinterpret_cast<float*>(ws + p.ws.u);
+    float* partial = reinterpret_cast<float*>(ws + p.ws.partial);
+    float* inv = reinterpret_cast<float*>(ws + p.ws.inv);
+    // decay factor f = fl(1 - fl(lr * wd)), float32 on the host
+    volatile float lrwd = lr * weight_decay;
+    const float decay = 1.0f - lrwd;
+
+    TRY_HIP(muon::launch_front(p, grads, momentum, u, partial, beta, nesterov, stream), "front");
+    TRY_HIP(muon::launch_norm(p, partial, inv, stream), "norm");
+    TRY_HIP(muon::launch_cast(p, u, inv, ws, ns_steps == 0 ? u : nullptr, stream), "cast");
+    if (ns_steps > 0)
+        TRY_HIP(muon::launch_newton_schulz(p, ws, u, ns_steps, stream), "newton-schulz");
+    TRY_HIP(muon::launch_apply(p, params, param_dtype, u, decay, lr, stream), "apply");
+    return MUON_OK;
+}
+
+int muon_momentum(const float* grads, float* momentum, float* u_out, int64_t n_state_elems,
+                  const muon_matrix_desc_t* descs, int64_t n, float beta, int nesterov,
+                  hipStream_t stream) {
+    Status st{MUON_OK, ""};
+    TRY(muon::check_desc_shapes(descs, n, &st));
+    TRY(check_flag(nesterov, "nesterov", &st));
+    TRY(muon::check_scalar(beta, "beta", &st));
+    if (n == 0) return MUON_OK;
+    TRY(check_null(grads, "grads", &st));
+    TRY(check_null(momentum, "momentum", &st));
+    TRY(check_null(u_out, "u_out", &st));
+    TRY(muon::check_state_ranges(descs, n, n_state_elems, "grads/momentum/u_out", &st));
+    const muon::Range ranges[3] = {{grads, size_t(n_state_elems) * 4, "grads"},
+                                   {momentum, size_t(n_state_elems) * 4, "momentum"},
+                                   {u_out, size_t(n_state_elems) * 4, "u_out"}};
+    TRY(muon::check_no_alias(ranges, 3, &st));
+    std::shared_ptr<const muon::PlanStore> plan;
+    TRY(muon::get_plan(descs, n, MUON_GEMM_BF16_MFMA, stream, &plan, &st));
+    const muon::PlanView& p = muon::view_of(*plan);
+    TRY_HIP(muon::launch_front(p, grads, momentum, u_out, nullptr, beta, nesterov, stream),
+            "front");
+    return MUON_OK;
+}
+
+int muon_orthogonalize(const float* u, float* o_out, int64_t n_elems,
+                       const muon_matrix_desc_t* descs, int64_t n, int ns_steps, int gemm_mode,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    Status st{MUON_OK, ""};
+    TRY(muon::check_desc_shapes(descs, n, &st));
+    TRY(check_mode(gemm_mode, &st));
+    TRY(check_ns_steps(ns_steps, &st));
+    if (n == 0) return MUON_OK;
+    TRY(check_null(u, "u", &st));
+    TRY(check_null(o_out, "o_out", &st));
+    TRY(muon::check_state_ranges(descs, n, n_elems, "u/o_out", &st));
+    const size_t need = muon::workspace_bytes_for(descs, n, gemm_mode);
+    TRY(check_workspace(workspace, workspace_bytes, need, &st));
+    const bool in_place = static_cast<const void*>(u) == static_cast<const void*>(o_out);
+    const muon::Range ranges[3] = {{u, size_t(n_elems) * 4, "u"},
+                                   {o_out, in_place ? 0 : size_t(n_elems) * 4, "o_out"},
+                                   {workspace, workspace_bytes, "workspace"}};
+    TRY(muon::check_no_alias(ranges, 3, &st));
+    std::shared_ptr<const muon::PlanStore> plan;
+    TRY(muon::get_plan(descs, n, gemm_mode, stream, &plan, &st));
+    const muon::PlanView& p = muon::view_of(*plan);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    float* partial = reinterpret_cast<float*>(ws + p.ws.partial);
+    float* inv = reinterpret_cast<float*>(ws + p.ws.inv);
+    TRY_HIP(muon::launch_sumsq(p, u, partial, stream), "sum of squares");
+    TRY_HIP(muon::launch_norm(p, partial, inv, stream), "norm");
+    TRY_HIP(muon::launch_cast(p, u, inv, ws, ns_steps == 0 ? o_out : nullptr, stream), "cast");
+    if (ns_steps > 0)
+        TRY_HIP(muon::launch_newton_schulz(p, ws, o_out, ns_steps, stream), "newton-schulz");
+    return MUON_OK;
+}
+
+int muon_apply(void* params, int param_dtype, int64_t n_param_elems, const float* updates,
+               int64_t n_update_elems, const muon_matrix_desc_t* descs, int64_t n, float lr,
+               float weight_decay, hipStream_t stream) {
+    Status st{MUON_OK, ""};
+    TRY(muon::check_desc_shapes(descs, n, &st));
+    TRY(muon::check_scalar(lr, "lr", &st));
+    TRY(muon::check_scalar(weight_decay, "weight_decay", &st));
+    if (param_dtype != MUON_DTYPE_F32 && param_dtype != MUON_DTYPE_BF16)
+        TRY(muon::check_param_ranges(descs, 0, 0, param_dtype, &st));
+    if (n == 0) return MUON_OK;
+    TRY(check_null(params, "params", &st));
+    TRY(check_null(updates, "updates", &st));
+    TRY(muon::check_state_ranges(descs, n, n_update_elems, "updates", &st));
+    TRY(muon::check_param_ranges(descs, n, n_param_elems, param_dtype, &st));
+    const muon::Range ranges[2] = {{params, param_bytes(param_dtype, n_param_elems), "params"},
+                                   {updates, size_t(n_update_elems) * 4, "updates"}};
+    TRY(muon::check_no_alias(ranges, 2, &st));
+    std::shared_ptr<const muon::PlanStore> plan;
+    TRY(muon::get_plan(descs, n, MUON_GEMM_BF16_MFMA, stream, &plan, &st));
+    volatile float lrwd = lr * weight_decay;
+    const float decay = 1.0f - lrwd;
+    TRY_HIP(muon::launch_apply(muon::view_of(*plan), params, param_dtype, updates, decay, lr,
+                               stream),
+            "apply");
+    return MUON_OK;
+}
+
+const char* muon_status_string(int status) {
+    switch (status) {
+        case MUON_OK: return "MUON_OK";
+        case MUON_ERR_NULL_POINTER: return "MUON_ERR_NULL_POINTER";
+        case MUON_ERR_BAD_SHAPE: return "MUON_ERR_BAD_SHAPE";
+        case MUON_ERR_OUT_OF_BOUNDS: return "MUON_ERR_OUT_OF_BOUNDS";
+        case MUON_ERR_MISALIGNED: return "MUON_ERR_MISALIGNED";
+        case MUON_ERR_OVERLAP: return "MUON_ERR_OVERLAP";
+        case MUON_ERR_ALIAS: return "MUON_ERR_ALIAS";
+        case MUON_ERR_BAD_ARG: return "MUON_ERR_BAD_ARG";
+        case MUON_ERR_WORKSPACE_TOO_SMALL: return "MUON_ERR_WORKSPACE_TOO_SMALL";
+        case MUON_ERR_HIP: return "MUON_ERR_HIP";
+        case MUON_ERR_INTERNAL: return "MUON_ERR_INTERNAL";
+        default: return "MUON_ERR_UNKNOWN";
+    }
+}
+
+const char* muon_last_error(void) { return t_last_error; }
+
+}  // extern "C"

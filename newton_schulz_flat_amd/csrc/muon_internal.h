@@ -1,0 +1,169 @@
+// Internal declarations shared by the host runtime (validation, plan, ABI)
+// and the gfx950 kernels of the flat-buffer Muon step.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <memory>
+
+#include <hip/hip_runtime_api.h>
+
+#include "muon_step.h"
+
+namespace muon {
+
+// ---------------------------------------------------------------- geometry
+
+// Elements handled by one workgroup of the elementwise kernels
+// (256 threads x 4 elements x 8 iterations).  One float partial sum of
+// squares is produced per chunk.
+constexpr int kEwThreads = 256;
+constexpr int kEwVec = 4;
+constexpr int kEwIters = 8;
+constexpr int64_t kEwChunk = int64_t(kEwThreads) * kEwVec * kEwIters;
+
+// Square tile of the normalize/cast/orient kernel.
+constexpr int kCastTile = 64;
+
+// Alignment of every workspace region, in bytes.
+constexpr size_t kWsAlign = 256;
+
+// Largest accepted matrix side and element count.
+constexpr int64_t kMaxSide = int64_t(1) << 20;
+constexpr int64_t kMaxNumel = int64_t(1) << 34;
+constexpr int kMaxNsSteps = 64;
+
+// Quintic Newton-Schulz coefficients and the norm epsilon.
+constexpr float kNsA = 3.4445f;
+constexpr float kNsB = -4.7750f;
+constexpr float kNsC = 2.0315f;
+constexpr float kNormEps = 1e-7f;
+
+// Per-matrix facts the kernels read (device copy lives in the plan tables).
+// All offsets are in elements.  "NS orientation": r = min(R, C) rows and
+// c = max(R, C) columns, padded with zeros to rp x cp (multiples of the GEMM
+// tile); tall matrices (R > C) are transposed into it.
+struct alignas(16) MatInfo {
+    int64_t off;        // start of the R x C matrix in the grads/momentum/U/O layout
+    int64_t numel;      // R * C
+    int64_t poff;       // start of slice 0 in params
+    int64_t pstride;    // slice stride in params
+    int64_t slice_len;  // numel / n_shards
+    int64_t x_off;      // start of X (rp x cp) in the X region; X^T (cp x rp) at the same
+                        // offset in each X^T region
+    int64_t g_off;      // start of the rp x rp Gram block in the A and B regions
+    int32_t R, C;       // original shape
+    int32_t r, c;       // NS-orientation shape
+    int32_t rp, cp;     // padded NS-orientation shape
+    int32_t tall;       // R > C
+    int32_t tile;       // GEMM tile size used for this matrix (64, 128 or 256)
+    int32_t chunk_begin, n_chunks;  // elementwise chunks / partial-sum slots
+    int32_t cast_begin, n_cast;     // normalize/cast tiles
+    float scale;        // (float) sqrt(max(1, R/C))
+    int32_t pad_[3];
+};
+static_assert(sizeof(MatInfo) == 128, "MatInfo layout");
+
+// One GEMM tile: matrix index and tile coordinates.
+struct alignas(16) GemmTile {
+    int32_t mat, ti, tj, pad_;
+};
+
+// Byte offsets of the workspace regions.
+struct WsLayout {
+    size_t u;        // float32 U / O, laid out like grads (state extent E)
+    size_t x;        // X, rp x cp per matrix
+    size_t xt[2];    // X^T ping-pong, cp x rp per matrix
+    size_t a, b;     // Gram matrices rp x rp per matrix
+    size_t partial;  // one float per elementwise chunk
+    size_t inv;      // one float per matrix
+    size_t total;
+};
+
+// Tiles of one GEMM tile size: symmetric (ti <= tj) and full rp x cp grids.
+struct TileClassDev {
+    int tile;
+    int n_sym;
+    int n_full;
+    const GemmTile* sym;   // device
+    const GemmTile* full;  // device
+};
+
+// A launch plan for one descriptor set, device and GEMM mode.
+struct PlanView {
+    int n;                      // matrices
+    int gemm_mode;
+    int64_t state_extent;       // max over descriptors of offset + numel
+    int64_t total_chunks;       // elementwise workgroups
+    int64_t total_cast;         // cast workgroups
+    WsLayout ws;
+    const MatInfo* mats_host;   // n entries
+    const MatInfo* mats;        // device, n entries
+    const int32_t* chunk_prefix;  // device, n + 1 entries
+    const int32_t* cast_prefix;   // device, n + 1 entries
+    int n_classes;
+    TileClassDev classes[3];
+};
+
+// --------------------------------------------------------------- validation
+
+struct Status {
+    int code;
+    char msg[512];
+};
+
+// Shapes, shard geometry and reserved fields of every descriptor.
+int check_desc_shapes(const muon_matrix_desc_t* d, int64_t n, Status* st);
+// Matrices inside [0, n_elems) of the float32 state layout, 16-byte aligned,
+// pairwise disjoint.
+int check_state_ranges(const muon_matrix_desc_t* d, int64_t n, int64_t n_elems, const char* what,
+                       Status* st);
+// Slices inside [0, n_param_elems) of params, 16-byte aligned, pairwise disjoint.
+int check_param_ranges(const muon_matrix_desc_t* d, int64_t n, int64_t n_param_elems,
+                       int param_dtype, Status* st);
+// Address ranges [ptr, ptr + bytes) of distinct buffers do not intersect.
+struct Range {
+    const void* ptr;
+    size_t bytes;
+    const char* name;
+};
+int check_no_alias(const Range* r, int count, Status* st);
+int check_scalar(float v, const char* name, Status* st);
+
+// --------------------------------------------------------------------- plan
+
+// Workspace bytes for a descriptor set (host only; shapes must be valid).
+size_t workspace_bytes_for(const muon_matrix_desc_t* d, int64_t n, int gemm_mode);
+
+// Owner of one plan's host tables and device memory.
+struct PlanStore;
+const PlanView& view_of(const PlanStore& s);
+
+// Cached plan for (device, gemm_mode, descriptors); builds and uploads it on
+// first use.  The shared pointer keeps the plan alive for the caller.
+int get_plan(const muon_matrix_desc_t* d, int64_t n, int gemm_mode, hipStream_t stream,
+             std::shared_ptr<const PlanStore>* out, Status* st);
+
+// ------------------------------------------------------------------ kernels
+
+// Momentum + orthogonalization input (+ per-chunk sum of squares of U).
+hipError_t launch_front(const PlanView& p, const float* grads, float* momentum, float* u,
+                        float* partial, float beta, int nesterov, hipStream_t s);
+// Per-chunk sum of squares of an existing U.
+hipError_t launch_sumsq(const PlanView& p, const float* u, float* partial, hipStream_t s);
+// Per-matrix 1 / (sqrt(sum of partials) + eps).
+hipError_t launch_norm(const PlanView& p, const float* partial, float* inv, hipStream_t s);
+// X0 = cast(U * inv) in NS orientation (and X0^T), zero padding; when
+// o_direct is non-null (ns_steps == 0) write O = s * X0 there instead.
+hipError_t launch_cast(const PlanView& p, const float* u, const float* inv, void* ws,
+                       float* o_direct, hipStream_t s);
+// ns_steps >= 1 Newton-Schulz iterations; the last writes O = s * X in the
+// original orientation to o.
+hipError_t launch_newton_schulz(const PlanView& p, void* ws, float* o, int ns_steps,
+                                hipStream_t s);
+// W <- fl(fl(W*f) - fl(lr*O)) scattered into the slices.
+hipError_t launch_apply(const PlanView& p, void* params, int param_dtype, const float* o,
+                        float decay, float lr, hipStream_t s);
+
+}  // namespace muon
