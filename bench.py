@@ -1,0 +1,209 @@
+"""Benchmark of the MI355X Muon step (one GPU).
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload llama] [--mode bf16]
+
+One "step" is one whole ``muon_step`` call (momentum + Nesterov input,
+Frobenius normalization, 5 Newton-Schulz iterations, decay + apply) over the
+workload's matrices, with every input already resident in HBM.  The default
+workload is one Llama-style decoder layer (Wq 4096x4096, Wk/Wv 1024x4096,
+Wo 4096x4096, gate/up 14336x4096, down 4096x14336; bfloat16 weights, float32
+gradients and momentum; synthetic seeded values).
+
+Prints one JSON line: matrices/s for the whole step, the Newton-Schulz
+algorithmic TFLOP/s and its fraction of the bf16 dense MFMA peak, the roofline
+of the dominant kernel (per-launch durations from HIP events recorded on the
+launch stream during the timed region), and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as wlm  # noqa: E402
+
+METRIC = "Muon step matrices/s; Newton-Schulz TFLOPS as % of bf16 MFMA peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense matrix peaks
+PEAK_HBM_GBS = 8000.0
+
+
+def ns_flops(r, c):
+    """Algorithmic flops of one iteration, by stage (triangles for the symmetric ones)."""
+    return {"a": r * (r + 1) * c, "b": r * r * (r + 1), "x": 2 * r * r * c}
+
+
+def stage_flops(wl, ns_steps):
+    tot = {"a": 0, "b": 0, "x": 0}
+    for d in wl.descs:
+        r, c = min(d.rows, d.cols), max(d.rows, d.cols)
+        for k, v in ns_flops(r, c).items():
+            tot[k] += v
+    return tot  # per iteration (one launch per stage and tile size)
+
+
+def elementwise_bytes(wl):
+    """Bytes each elementwise kernel must move, per step."""
+    n = wl.numel()
+    wb = 2 if wl.param_dtype == "bf16" else 4
+    return {"front": 16 * n,           # G read, M read + write, U write (float32)
+            "cast": 4 * n + 2 * 2 * n,  # U read, X0 and X0^T written (bf16)
+            "apply": 4 * n + 2 * wb * n}  # O read, W read + write
+
+
+def cpu_baseline(wl, budget_s=20.0):
+    """Oracle (fp64 NumPy) step time on a bounded sample, scaled to the workload."""
+    import numpy as np
+    from oracle import muon_oracle as mo
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    h = wlm.HYPER
+    order = sorted(range(wl.n), key=lambda i: wl.descs[i].rows * wl.descs[i].cols)
+    picked, spent, sample_flops = [], 0.0, 0.0
+    for i in order:
+        d = wl.descs[i]
+        r, c = min(d.rows, d.cols), max(d.rows, d.cols)
+        rng = np.random.default_rng([wlm.seed_of(wl.name, i, 0)])
+        w = rng.standard_normal((d.rows, d.cols)) * wl.w_std
+        g = rng.standard_normal((d.rows, d.cols)) * wl.g_std
+        m = np.zeros_like(g)
+        t0 = time.perf_counter()
+        mo.step_matrix(w, g, m, lr=mo.as_f32_value(h["lr"]),
+                       weight_decay=mo.as_f32_value(h["weight_decay"]),
+                       beta=mo.as_f32_value(h["beta"]), nesterov=True, ns_steps=h["ns_steps"])
+        spent += time.perf_counter() - t0
+        sample_flops += sum(ns_flops(r, c).values()) * h["ns_steps"]
+        picked.append(f"{wl.names[i]} {d.rows}x{d.cols}")
+        if spent > budget_s / 2:
+            break
+    total_flops = sum(stage_flops(wl, h["ns_steps"]).values()) * h["ns_steps"]
+    est = spent * total_flops / sample_flops
+    return {"value": wl.n / est, "unit": "matrices/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"fp64 NumPy oracle step of {', '.join(picked)} ({spent:.1f} s), "
+                       f"scaled by Newton-Schulz flops to all {wl.n} matrices")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama", choices=wlm.WORKLOADS)
+    ap.add_argument("--mode", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs the Muon step on one GPU only; the multi-GPU "
+              "owner-compute path is not built, so --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import newton_schulz_flat_amd as nsf
+    if not os.path.exists(nsf.LIB_PATH):
+        from newton_schulz_flat_amd import build
+        build.build()
+    nsf.load_library()
+
+    h = wlm.HYPER
+    wl = wlm.make_workload(args.workload)
+    torch.cuda.set_device(0)
+    params, grads, mom = wlm.make_tensors(wl, "cuda:0")
+    ws = nsf.workspace_for(wl.descs, args.mode, grads.device)
+
+    def step():
+        nsf.muon_step(params, grads, mom, wl.descs, h["lr"], h["weight_decay"], h["beta"],
+                      nesterov=h["nesterov"], ns_steps=h["ns_steps"], mode=args.mode,
+                      workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nsf.muon_profile_begin()
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    kernels = nsf.muon_profile_end()
+    ms = ev0.elapsed_time(ev1) / args.steps
+
+    fl = stage_flops(wl, h["ns_steps"])
+    ns_ms = sum(v[0] for k, v in kernels.items() if k.startswith("ns_")) / args.steps
+    ns_alg = sum(fl.values()) * h["ns_steps"]
+    ns_tflops = ns_alg / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else 0.0
+    ew = elementwise_bytes(wl)
+
+    # dominant kernel = largest total time; its algorithmic work per launch
+    name, (tot_ms, launches) = max(kernels.items(), key=lambda kv: kv[1][0])
+    avg_s = tot_ms / launches * 1e-3
+    if name.startswith("ns_"):
+        stage = name.split("_")[1]
+        same = [k for k in kernels if k.startswith(f"ns_{stage}_")]
+        if len(same) == 1:
+            work = fl[stage]
+        else:  # several tile sizes: attribute this stage's flops by measured time share
+            work = fl[stage] * tot_ms / sum(kernels[k][0] for k in same)
+        roof = {"kernel": name, "bound": "mfma", "achieved": work / avg_s / 1e12,
+                "peak": PEAK_TFLOPS[args.mode], "unit": "TFLOP/s",
+                "work_per_launch": work, "avg_launch_ms": avg_s * 1e3}
+    else:
+        work = ew.get(name, 0)
+        roof = {"kernel": name, "bound": "hbm", "achieved": work / avg_s / 1e9,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "work_per_launch": work,
+                "avg_launch_ms": avg_s * 1e3}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+
+    per_kernel = {k: {"ms_per_step": v[0] / args.steps, "launches_per_step": v[1] / args.steps}
+                  for k, v in sorted(kernels.items())}
+    for k in ("front", "cast", "apply"):
+        if k in kernels:
+            per_kernel[k]["GB/s"] = ew[k] / (kernels[k][0] / kernels[k][1] * 1e-3) / 1e9
+            per_kernel[k]["frac_hbm"] = per_kernel[k]["GB/s"] / PEAK_HBM_GBS
+
+    out = {
+        "metric": METRIC,
+        "value": wl.n * 1e3 / ms,
+        "unit": "matrices/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if args.mode == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": {"llama": "llama-layer"}.get(wl.name, wl.name),
+                   "matrices": wl.n, "elements": wl.numel(), "param_dtype": wl.param_dtype,
+                   "gemm_mode": args.mode, "ns_steps": h["ns_steps"], "lr": h["lr"],
+                   "weight_decay": h["weight_decay"], "beta": h["beta"], "nesterov": True,
+                   "parallelism": "single-gpu"},
+        "ns_tflops": ns_tflops,
+        "ns_frac_of_peak": ns_tflops / PEAK_TFLOPS[args.mode],
+        "ns_ms_per_step": ns_ms,
+        "roofline": roof,
+        "kernels": per_kernel,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -159,6 +159,26 @@ int muon_apply(void* params, int param_dtype, int64_t n_param_elems, const float
                int64_t n_update_elems, const muon_matrix_desc_t* descs, int64_t n, float lr,
                float weight_decay, hipStream_t stream);
 
+/* Kernel timing, a profiling aid (not part of the step's semantics).
+ * Between muon_profile_begin() and muon_profile_end(), every kernel the
+ * library launches, from any thread, is bracketed by two HIP events recorded
+ * on the launch's own stream.  muon_profile_end() stops recording, waits for
+ * the recorded events, and aggregates elapsed time by kernel name into `out`
+ * (at most max_entries rows, host memory; *n_entries receives the number of
+ * distinct kernels, which may exceed max_entries).  Names are
+ * "front", "sumsq", "norm", "cast", "apply" and "ns_<stage>_t<tile>_<type>"
+ * for the Newton-Schulz products (stage a: X X^T, b: b A + c A A, x: a X + B X;
+ * tile 64/128/256; type bf16/f32).  Events come from a pool the library owns;
+ * when timing is off the only cost is one flag test per launch. */
+typedef struct muon_kernel_time {
+    char name[48];
+    double total_ms;   /* sum of the launches' event-to-event times */
+    int64_t launches;
+} muon_kernel_time_t;
+
+int muon_profile_begin(void);
+int muon_profile_end(muon_kernel_time_t* out, int max_entries, int* n_entries);
+
 /* Static name of a status code ("MUON_OK", "MUON_ERR_BAD_SHAPE", ...). */
 const char* muon_status_string(int status);
 

@@ -37,7 +37,8 @@ _MODES = {"bf16": MUON_GEMM_BF16_MFMA, "f32": MUON_GEMM_F32}
 
 #: C names of every exported entry point (mirrors include/muon_step.h).
 EXPORTS = ("muon_workspace_bytes", "muon_step", "muon_momentum", "muon_orthogonalize",
-           "muon_apply", "muon_status_string", "muon_last_error")
+           "muon_apply", "muon_profile_begin", "muon_profile_end", "muon_status_string",
+           "muon_last_error")
 
 
 class MatrixDescC(ctypes.Structure):
@@ -46,6 +47,13 @@ class MatrixDescC(ctypes.Structure):
     _fields_ = [("offset", ctypes.c_int64), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
                 ("param_offset", ctypes.c_int64), ("shard_stride", ctypes.c_int64),
                 ("n_shards", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class KernelTimeC(ctypes.Structure):
+    """``muon_kernel_time_t``."""
+
+    _fields_ = [("name", ctypes.c_char * 48), ("total_ms", ctypes.c_double),
+                ("launches", ctypes.c_int64)]
 
 
 class MuonError(RuntimeError):
@@ -78,12 +86,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.muon_momentum.argtypes = [p, p, p, i64, dp, i64, f32, i32, p]
     lib.muon_orthogonalize.argtypes = [p, p, i64, dp, i64, i32, i32, p, sz, p]
     lib.muon_apply.argtypes = [p, i32, i64, p, i64, dp, i64, f32, f32, p]
+    lib.muon_profile_begin.argtypes = []
+    lib.muon_profile_end.argtypes = [ctypes.POINTER(KernelTimeC), i32, ctypes.POINTER(i32)]
     lib.muon_status_string.argtypes = [i32]
     lib.muon_status_string.restype = ctypes.c_char_p
     lib.muon_last_error.argtypes = []
     lib.muon_last_error.restype = ctypes.c_char_p
     for name in ("muon_workspace_bytes", "muon_step", "muon_momentum", "muon_orthogonalize",
-                 "muon_apply"):
+                 "muon_apply", "muon_profile_begin", "muon_profile_end"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -218,3 +228,18 @@ def muon_apply(params, updates, descs, lr: float, weight_decay: float):
     check(lib.muon_apply(params.data_ptr(), dt, params.numel(), updates.data_ptr(),
                          updates.numel(), descs_array(descs), _count(descs), lr, weight_decay,
                          _stream(updates)))
+
+
+def muon_profile_begin() -> None:
+    """Start timing every kernel launch with HIP events on its stream."""
+    check(load_library().muon_profile_begin())
+
+
+def muon_profile_end() -> dict:
+    """Stop timing; returns {kernel name: (total_ms, launches)}."""
+    lib = load_library()
+    rows = (KernelTimeC * 64)()
+    count = ctypes.c_int(0)
+    check(lib.muon_profile_end(rows, 64, ctypes.byref(count)))
+    return {rows[k].name.decode(): (rows[k].total_ms, rows[k].launches)
+            for k in range(min(count.value, 64))}

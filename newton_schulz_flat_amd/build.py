@@ -25,6 +25,7 @@ SOURCES = [
     "muon_abi.cpp",
     "muon_validate.cpp",
     "muon_plan.cpp",
+    "muon_profile.cpp",
     "k_elementwise.hip",
     "k_norm_cast.hip",
     "k_ns_gemm.hip",

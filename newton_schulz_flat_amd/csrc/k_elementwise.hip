@@ -164,6 +164,7 @@ __global__ __launch_bounds__(kEwThreads) void apply_kernel(
 hipError_t launch_front(const PlanView& p, const float* grads, float* momentum, float* u,
                         float* partial, float beta, int nesterov, hipStream_t s) {
     if (p.total_chunks == 0) return hipSuccess;
+    LaunchTimer timer("front", s);
     front_kernel<0><<<dim3(unsigned(p.total_chunks)), dim3(kEwThreads), 0, s>>>(
         p.mats, p.chunk_prefix, p.n, grads, momentum, u, partial, beta, nesterov);
     return hipGetLastError();
@@ -171,6 +172,7 @@ hipError_t launch_front(const PlanView& p, const float* grads, float* momentum, 
 
 hipError_t launch_sumsq(const PlanView& p, const float* u, float* partial, hipStream_t s) {
     if (p.total_chunks == 0) return hipSuccess;
+    LaunchTimer timer("sumsq", s);
     front_kernel<1><<<dim3(unsigned(p.total_chunks)), dim3(kEwThreads), 0, s>>>(
         p.mats, p.chunk_prefix, p.n, nullptr, nullptr, const_cast<float*>(u), partial, 0.f, 0);
     return hipGetLastError();
@@ -179,6 +181,7 @@ hipError_t launch_sumsq(const PlanView& p, const float* u, float* partial, hipSt
 hipError_t launch_apply(const PlanView& p, void* params, int param_dtype, const float* o,
                         float decay, float lr, hipStream_t s) {
     if (p.total_chunks == 0) return hipSuccess;
+    LaunchTimer timer("apply", s);
     const dim3 grid{static_cast<unsigned>(p.total_chunks)}, block{kEwThreads};
     if (param_dtype == MUON_DTYPE_BF16)
         apply_kernel<uint16_t><<<grid, block, 0, s>>>(p.mats, p.chunk_prefix, p.n,

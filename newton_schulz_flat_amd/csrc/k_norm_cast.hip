@@ -105,6 +105,7 @@ __global__ __launch_bounds__(256) void cast_kernel(const MatInfo* __restrict__ m
 
 hipError_t launch_norm(const PlanView& p, const float* partial, float* inv, hipStream_t s) {
     if (p.n == 0) return hipSuccess;
+    LaunchTimer timer("norm", s);
     norm_kernel<<<dim3(unsigned(p.n)), dim3(kNormThreads), 0, s>>>(p.mats, partial, inv);
     return hipGetLastError();
 }
@@ -112,6 +113,7 @@ hipError_t launch_norm(const PlanView& p, const float* partial, float* inv, hipS
 hipError_t launch_cast(const PlanView& p, const float* u, const float* inv, void* ws,
                        float* o_direct, hipStream_t s) {
     if (p.total_cast == 0) return hipSuccess;
+    LaunchTimer timer("cast", s);
     unsigned char* w = static_cast<unsigned char*>(ws);
     const dim3 grid{static_cast<unsigned>(p.total_cast)}, block{256};
     if (p.gemm_mode == MUON_GEMM_F32)

@@ -87,6 +87,38 @@ __device__ __forceinline__ void store4(uint16_t* p, const float v[4]) {
     *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
 }
 
+// Quad transpose: lanes 4m+s (s = 0..3, same half-wave) each hold one column
+// of a 4 x 4 block, v[t] = M[t][s]; afterwards lane 4m+s holds row s,
+// w[t] = M[s][t].  Two DPP butterflies (xor 2, then xor 1) and a final
+// lane-dependent permutation.
+__device__ __forceinline__ float dpp_xor1(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ void quad_transpose(const float v[4], float w[4], int s) {
+    const bool hi2 = (s & 2) != 0, hi1 = (s & 1) != 0;
+    // stage 1: keep rows rb, rb+1 (rb = s & 2) of columns s and s^2
+    const float y0 = dpp_xor2(hi2 ? v[0] : v[2]);
+    const float y1 = dpp_xor2(hi2 ? v[1] : v[3]);
+    const float c0 = hi2 ? v[2] : v[0], c1 = hi2 ? v[3] : v[1];
+    // c0 = M[rb][s], c1 = M[rb+1][s], y0 = M[rb][s^2], y1 = M[rb+1][s^2]
+    // stage 2: keep row s of columns s and s^2, receive columns s^1 and s^3
+    const float z0 = dpp_xor1(hi1 ? c0 : c1);
+    const float z1 = dpp_xor1(hi1 ? y0 : y1);
+    const float k0 = hi1 ? c1 : c0, k1 = hi1 ? y1 : y0;
+    // M[s][s] = k0, M[s][s^1] = z0, M[s][s^2] = k1, M[s][s^3] = z1
+    const float e0 = hi1 ? z0 : k0, e1 = hi1 ? k0 : z0;  // columns (s&2), (s&2)+1
+    const float e2 = hi1 ? z1 : k1, e3 = hi1 ? k1 : z1;  // columns (s&2)^2, ((s&2)^2)+1
+    w[0] = hi2 ? e2 : e0;
+    w[1] = hi2 ? e3 : e1;
+    w[2] = hi2 ? e0 : e2;
+    w[3] = hi2 ? e1 : e3;
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 template <int TILE, bool BF16, int STAGE>
 __global__ __launch_bounds__(256) void ns_gemm_kernel(NsArgs args) {
     using TE = std::conditional_t<BF16, uint16_t, float>;
@@ -94,6 +126,7 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(NsArgs args) {
     constexpr int kEs = BF16 ? 2 : 4;
     constexpr int kBk = kRowBytes / kEs;  // K elements per block
     constexpr int kNf = G::kNf;
+    constexpr int kL = G::kLoads;
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * 2 * G::kOp];
 
     const GemmTile tile = args.tiles[blockIdx.x];
@@ -128,28 +161,16 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(NsArgs args) {
     const int wm = wave >> 1, wn = wave & 1;
     const int lr = lane & 31, hk = lane >> 5;
 
-    uint4 rp_[G::kLoads], rq_[G::kLoads];
-    auto gload = [&](int kb) {
-#pragma unroll
-        for (int l = 0; l < G::kLoads; ++l) {
-            const int c = l * 256 + tid;
-            const int row = c >> 3, col = (c & 7) * (16 / kEs);
-            const int64_t at = int64_t(row) * ld + int64_t(kb) * kBk + col;
-            rp_[l] = *reinterpret_cast<const uint4*>(P + at);
-            rq_[l] = *reinterpret_cast<const uint4*>(Q + at);
-        }
-    };
-    auto lstore = [&](int buf) {
-        unsigned char* lp = lds + buf * 2 * G::kOp;
-        unsigned char* lq = lp + G::kOp;
-#pragma unroll
-        for (int l = 0; l < G::kLoads; ++l) {
-            const int c = l * 256 + tid;
-            const int row = c >> 3, col16 = c & 7;
-            *reinterpret_cast<uint4*>(lp + row * kLdsStride + col16 * 16) = rp_[l];
-            *reinterpret_cast<uint4*>(lq + row * kLdsStride + col16 * 16) = rq_[l];
-        }
-    };
+    // Global -> LDS staging: thread tid moves 16-byte chunk (tid & 7) of rows
+    // (tid >> 3) + 32 l, l = 0..kL-1, of each operand's K block.
+    const int lrow = tid >> 3, lchunk = tid & 7;
+    const TE* gp = P + int64_t(lrow) * ld + lchunk * (16 / kEs);
+    const TE* gq = Q + int64_t(lrow) * ld + lchunk * (16 / kEs);
+    const int64_t rstep = int64_t(32) * ld;
+    const int lds_st = lrow * kLdsStride + lchunk * 16;
+    // Fragment reads: row lr of each 32-row fragment, bytes [hk*64, hk*64 + 64).
+    const int fa_off = (wm * G::kWt + lr) * kLdsStride + hk * 64;
+    const int fb_off = G::kOp + (wn * G::kWt + lr) * kLdsStride + hk * 64;
 
     f32x16 acc[kNf][kNf];
 #pragma unroll
@@ -159,114 +180,177 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(NsArgs args) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    const int nkb = K / kBk;
-    gload(0);
-    lstore(0);
+    u32x4 pa[kL], pb[kL];
+#pragma unroll
+    for (int l = 0; l < kL; ++l) {
+        pa[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep);
+        pb[l] = *reinterpret_cast<const u32x4*>(gq + l * rstep);
+    }
+#pragma unroll
+    for (int l = 0; l < kL; ++l) {
+        *reinterpret_cast<u32x4*>(lds + lds_st + l * 32 * kLdsStride) = pa[l];
+        *reinterpret_cast<u32x4*>(lds + G::kOp + lds_st + l * 32 * kLdsStride) = pb[l];
+    }
     __syncthreads();
+
+    const int nkb = K / kBk;
     for (int kb = 0; kb < nkb; ++kb) {
-        const int cur = kb & 1;
-        if (kb + 1 < nkb) gload(kb + 1);
-        const unsigned char* lp = lds + cur * 2 * G::kOp;
-        const unsigned char* lq = lp + G::kOp;
-        // Lane (lr, hk) reads row lr of each fragment, bytes [hk*64, hk*64+64) of the
-        // K block, 16 bytes per step q.  P and Q use the same K assignment, so the
-        // products cover every K index of the block exactly once.
+        const bool more = kb + 1 < nkb;
+        if (more) {
+            const int64_t k0 = int64_t(kb + 1) * kBk;
+#pragma unroll
+            for (int l = 0; l < kL; ++l) {
+                pa[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep + k0);
+                pb[l] = *reinterpret_cast<const u32x4*>(gq + l * rstep + k0);
+            }
+        }
+        const unsigned char* buf = lds + (kb & 1) * 2 * G::kOp;
+        u32x4 fa[2][kNf], fb[2][kNf];
+#pragma unroll
+        for (int i = 0; i < kNf; ++i) {
+            fa[0][i] = *reinterpret_cast<const u32x4*>(buf + fa_off + i * 32 * kLdsStride);
+            fb[0][i] = *reinterpret_cast<const u32x4*>(buf + fb_off + i * 32 * kLdsStride);
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            uint4 fa[kNf], fb[kNf];
+            const int cur = q & 1;
+            if (q < 3) {
 #pragma unroll
-            for (int i = 0; i < kNf; ++i)
-                fa[i] = *reinterpret_cast<const uint4*>(
-                    lp + (wm * G::kWt + i * 32 + lr) * kLdsStride + hk * 64 + q * 16);
-#pragma unroll
-            for (int j = 0; j < kNf; ++j)
-                fb[j] = *reinterpret_cast<const uint4*>(
-                    lq + (wn * G::kWt + j * 32 + lr) * kLdsStride + hk * 64 + q * 16);
+                for (int i = 0; i < kNf; ++i) {
+                    fa[cur ^ 1][i] = *reinterpret_cast<const u32x4*>(
+                        buf + fa_off + i * 32 * kLdsStride + (q + 1) * 16);
+                    fb[cur ^ 1][i] = *reinterpret_cast<const u32x4*>(
+                        buf + fb_off + i * 32 * kLdsStride + (q + 1) * 16);
+                }
+            }
             if constexpr (BF16) {
 #pragma unroll
                 for (int i = 0; i < kNf; ++i)
 #pragma unroll
                     for (int j = 0; j < kNf; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8, fa[i]), __builtin_bit_cast(bf16x8, fb[j]),
-                            acc[i][j], 0, 0, 0);
+                            __builtin_bit_cast(bf16x8, fa[cur][i]),
+                            __builtin_bit_cast(bf16x8, fb[cur][j]), acc[i][j], 0, 0, 0);
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
 #pragma unroll
                     for (int i = 0; i < kNf; ++i)
 #pragma unroll
-                        for (int j = 0; j < kNf; ++j) {
-                            const uint32_t ua = e == 0 ? fa[i].x : e == 1 ? fa[i].y : e == 2 ? fa[i].z : fa[i].w;
-                            const uint32_t ub = e == 0 ? fb[j].x : e == 1 ? fb[j].y : e == 2 ? fb[j].z : fb[j].w;
+                        for (int j = 0; j < kNf; ++j)
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                                __uint_as_float(ua), __uint_as_float(ub), acc[i][j], 0, 0, 0);
-                        }
+                                __uint_as_float(fa[cur][i][e]), __uint_as_float(fb[cur][j][e]),
+                                acc[i][j], 0, 0, 0);
             }
         }
-        if (kb + 1 < nkb) lstore(cur ^ 1);
+        if (more) {
+            unsigned char* nb = lds + ((kb + 1) & 1) * 2 * G::kOp;
+#pragma unroll
+            for (int l = 0; l < kL; ++l) {
+                *reinterpret_cast<u32x4*>(nb + lds_st + l * 32 * kLdsStride) = pa[l];
+                *reinterpret_cast<u32x4*>(nb + G::kOp + lds_st + l * 32 * kLdsStride) = pb[l];
+            }
+        }
         __syncthreads();
     }
 
     // Epilogue.  Lane (lr, hk) of fragment (i, j) holds, for g = 0..3, the
-    // outputs at rows rbase + 0..3 (rbase = i*32 + g*8 + hk*4) and column lr.
+    // outputs at rows gi + 0..3 (gi = tile row + i*32 + g*8 + hk*4) of column gj.
+    // Column-oriented stores take those 4 values as one vector; row-oriented
+    // stores first exchange them across the lane quad so that lane s of the
+    // quad holds row gi + s, columns gj - s .. gj - s + 3.
+    const int s4 = lr & 3;
+    const int row0 = ti * TILE + wm * G::kWt + hk * 4;
+    const int col0 = tj * TILE + wn * G::kWt + lr;
     const float ca = args.ca, cb = args.cb, cc = args.cc;
+    if (STAGE != kStageX || !args.last) {
+        TE* out_n;  // row-oriented destination, leading dimension ld_n
+        TE* out_t;  // column-oriented destination, leading dimension ld_t
+        int ld_n, ld_t;
+        if (STAGE == kStageX) {
+            out_n = static_cast<TE*>(args.x) + mt.x_off;
+            out_t = static_cast<TE*>(args.xt_next) + mt.x_off;
+            ld_n = cp;
+            ld_t = rp;
+        } else {
+            out_n = static_cast<TE*>(STAGE == kStageA ? args.ga : args.gb) + mt.g_off;
+            out_t = out_n;
+            ld_n = rp;
+            ld_t = rp;
+        }
+        const bool write_t = STAGE == kStageX || ti != tj;
+        const TE* opnd = nullptr;  // epilogue operand, read column-oriented
+        if (STAGE == kStageB) opnd = static_cast<const TE*>(args.ga) + mt.g_off;
+        if (STAGE == kStageX) opnd = static_cast<const TE*>(args.xt_cur) + mt.x_off;
 #pragma unroll
-    for (int i = 0; i < kNf; ++i) {
+        for (int i = 0; i < kNf; ++i) {
 #pragma unroll
-        for (int j = 0; j < kNf; ++j) {
-            const int gj = tj * TILE + wn * G::kWt + j * 32 + lr;
+            for (int j = 0; j < kNf; ++j) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int gi = ti * TILE + wm * G::kWt + i * 32 + g * 8 + hk * 4;
-                float v[4];
+                for (int g = 0; g < 4; ++g) {
+                    const int gi = row0 + i * 32 + g * 8;
+                    const int gj = col0 + j * 32;
+                    float v[4];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) v[t] = acc[i][j][g * 4 + t];
-                if (STAGE == kStageA || STAGE == kStageB) {
-                    TE* out = static_cast<TE*>(STAGE == kStageA ? args.ga : args.gb) + mt.g_off;
-                    if (STAGE == kStageB) {
-                        // A is symmetric: A[gi+t][gj] = A[gj][gi+t], 4 consecutive elements
-                        float av[4];
-                        load4(static_cast<const TE*>(args.ga) + mt.g_off + int64_t(gj) * rp + gi, av);
+                    for (int t = 0; t < 4; ++t) v[t] = acc[i][j][g * 4 + t];
+                    if (STAGE != kStageA) {
+                        float ov[4];
+                        load4(opnd + int64_t(gj) * rp + gi, ov);
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) v[t] = cb * av[t] + cc * v[t];
+                        for (int t = 0; t < 4; ++t)
+                            v[t] = STAGE == kStageB ? cb * ov[t] + cc * v[t] : ca * ov[t] + v[t];
                     }
+                    if (write_t) store4(out_t + int64_t(gj) * ld_t + gi, v);
+                    float w[4];
+                    quad_transpose(v, w, s4);
+                    store4(out_n + int64_t(gi + s4) * ld_n + (gj - s4), w);
+                }
+            }
+        }
+    } else {
+        // Last iteration: O = fl(s * X) in the matrix's own R x C layout.
+        const TE* xt = static_cast<const TE*>(args.xt_cur) + mt.x_off;
+        float* om = args.o + mt.off;
+        const float sc = mt.scale;
+        const int r = mt.r, c = mt.c;
+        const bool tall = mt.tall != 0;
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) store_e(out + int64_t(gi + t) * rp + gj, v[t]);
-                    if (ti != tj) store4(out + int64_t(gj) * rp + gi, v);
-                } else {
-                    // X[gi+t][gj] = X^T[gj][gi+t]
-                    float xv[4];
-                    load4(static_cast<const TE*>(args.xt_cur) + mt.x_off + int64_t(gj) * rp + gi, xv);
+        for (int i = 0; i < kNf; ++i) {
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) v[t] = ca * xv[t] + v[t];
-                    if (!args.last) {
-                        TE* xo = static_cast<TE*>(args.x) + mt.x_off;
+            for (int j = 0; j < kNf; ++j) {
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) store_e(xo + int64_t(gi + t) * cp + gj, v[t]);
-                        store4(static_cast<TE*>(args.xt_next) + mt.x_off + int64_t(gj) * rp + gi, v);
-                    } else {
-                        float* om = args.o + mt.off;
-                        const float s = mt.scale;
-                        if (!mt.tall) {
-                            // O is r x c (R = r, C = c): O[gi+t][gj]
-                            if (gj < mt.c) {
+                for (int g = 0; g < 4; ++g) {
+                    const int gi = row0 + i * 32 + g * 8;
+                    const int gj = col0 + j * 32;
+                    float v[4], xv[4];
+                    load4(xt + int64_t(gj) * rp + gi, xv);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) v[t] = sc * (ca * xv[t] + acc[i][j][g * 4 + t]);
+                    if (tall) {
+                        // O is c x r: O[gj][gi + t], 4 consecutive elements
+                        if (gj < c) {
+                            float* dst = om + int64_t(gj) * r + gi;
+                            if (gi + 3 < r && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+                                store4(dst, v);
+                            } else {
 #pragma unroll
                                 for (int t = 0; t < 4; ++t)
-                                    if (gi + t < mt.r) om[int64_t(gi + t) * mt.c + gj] = s * v[t];
+                                    if (gi + t < r) dst[t] = v[t];
                             }
-                        } else {
-                            // O is c x r (R = c, C = r): O[gj][gi+t], 4 consecutive elements
-                            if (gj < mt.c) {
-                                float* dst = om + int64_t(gj) * mt.r + gi;
-                                const float w4[4] = {s * v[0], s * v[1], s * v[2], s * v[3]};
-                                if (gi + 3 < mt.r && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-                                    store4(dst, w4);
-                                } else {
+                        }
+                    } else {
+                        // O is r x c: after the quad exchange, O[gi + s][gj - s + t]
+                        float w[4];
+                        quad_transpose(v, w, s4);
+                        const int orow = gi + s4, ocol = gj - s4;
+                        if (orow < r) {
+                            float* dst = om + int64_t(orow) * c + ocol;
+                            if (ocol + 3 < c && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+                                store4(dst, w);
+                            } else {
 #pragma unroll
-                                    for (int t = 0; t < 4; ++t)
-                                        if (gi + t < mt.r) dst[t] = w4[t];
-                                }
+                                for (int t = 0; t < 4; ++t)
+                                    if (ocol + t < c) dst[t] = w[t];
                             }
                         }
                     }
@@ -277,8 +361,24 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(NsArgs args) {
 }
 
 template <int TILE, bool BF16>
+const char* stage_name(int stage) {
+    static const char* const names[3] = {
+        TILE == 256 ? (BF16 ? "ns_a_t256_bf16" : "ns_a_t256_f32")
+                    : TILE == 128 ? (BF16 ? "ns_a_t128_bf16" : "ns_a_t128_f32")
+                                  : (BF16 ? "ns_a_t64_bf16" : "ns_a_t64_f32"),
+        TILE == 256 ? (BF16 ? "ns_b_t256_bf16" : "ns_b_t256_f32")
+                    : TILE == 128 ? (BF16 ? "ns_b_t128_bf16" : "ns_b_t128_f32")
+                                  : (BF16 ? "ns_b_t64_bf16" : "ns_b_t64_f32"),
+        TILE == 256 ? (BF16 ? "ns_x_t256_bf16" : "ns_x_t256_f32")
+                    : TILE == 128 ? (BF16 ? "ns_x_t128_bf16" : "ns_x_t128_f32")
+                                  : (BF16 ? "ns_x_t64_bf16" : "ns_x_t64_f32")};
+    return names[stage];
+}
+
+template <int TILE, bool BF16>
 hipError_t launch_stage(int stage, int n_tiles, const NsArgs& a, hipStream_t s) {
     if (n_tiles == 0) return hipSuccess;
+    LaunchTimer timer(stage_name<TILE, BF16>(stage), s);
     const dim3 grid{static_cast<unsigned>(n_tiles)}, block{256};
     switch (stage) {
         case kStageA: ns_gemm_kernel<TILE, BF16, kStageA><<<grid, block, 0, s>>>(a); break;

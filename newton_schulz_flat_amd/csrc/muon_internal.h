@@ -145,6 +145,23 @@ const PlanView& view_of(const PlanStore& s);
 int get_plan(const muon_matrix_desc_t* d, int64_t n, int gemm_mode, hipStream_t stream,
              std::shared_ptr<const PlanStore>* out, Status* st);
 
+// ---------------------------------------------------------------- profiling
+
+// Brackets one kernel launch with HIP events on its stream while kernel
+// timing is on (muon_profile_begin / muon_profile_end); a no-op otherwise.
+class LaunchTimer {
+  public:
+    LaunchTimer(const char* name, hipStream_t s);
+    ~LaunchTimer();
+    LaunchTimer(const LaunchTimer&) = delete;
+    LaunchTimer& operator=(const LaunchTimer&) = delete;
+
+  private:
+    const char* name_;
+    hipStream_t stream_;
+    void* start_ = nullptr;  // hipEvent_t when active
+};
+
 // ------------------------------------------------------------------ kernels
 
 // Momentum + orthogonalization input (+ per-chunk sum of squares of U).
