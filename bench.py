@@ -101,6 +101,9 @@ def main():
     ap.add_argument("--workload", default="llama", choices=wlm.WORKLOADS)
     ap.add_argument("--mode", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (calibrates the "
+                         "HBM byte counters of a profiler run) and exit")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -109,6 +112,16 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n}))
+        return
+
     import newton_schulz_flat_amd as nsf
     if not os.path.exists(nsf.LIB_PATH):
         from newton_schulz_flat_amd import build

@@ -193,65 +193,85 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(NsArgs args) {
     }
     __syncthreads();
 
+    // Main loop.  One K block is a single basic block whose instruction order
+    // is fixed with scheduling barriers: each MFMA is followed by at most one
+    // memory instruction, so the matrix pipe keeps issuing while
+    //   q = 0: the 2*kL global loads of the block after next are issued,
+    //   q < 3: the fragments of step q+1 are read from LDS (double-buffered
+    //          registers),
+    //   q = 3: the prefetched block is written to the other LDS buffer.
+    // The last block reloads itself (a valid, unused copy) to stay branch free.
     const int nkb = K / kBk;
+    constexpr int kMfma = kNf * kNf;  // MFMAs per step q (per K sub-step for bf16)
+    u32x4 fa[2][kNf], fb[2][kNf];
+#pragma unroll
+    for (int i = 0; i < kNf; ++i) {
+        fa[0][i] = *reinterpret_cast<const u32x4*>(lds + fa_off + i * 32 * kLdsStride);
+        fb[0][i] = *reinterpret_cast<const u32x4*>(lds + fb_off + i * 32 * kLdsStride);
+    }
     for (int kb = 0; kb < nkb; ++kb) {
-        const bool more = kb + 1 < nkb;
-        if (more) {
-            const int64_t k0 = int64_t(kb + 1) * kBk;
-#pragma unroll
-            for (int l = 0; l < kL; ++l) {
-                pa[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep + k0);
-                pb[l] = *reinterpret_cast<const u32x4*>(gq + l * rstep + k0);
-            }
-        }
+        const int64_t k0 = int64_t(kb + 1 < nkb ? kb + 1 : kb) * kBk;
         const unsigned char* buf = lds + (kb & 1) * 2 * G::kOp;
-        u32x4 fa[2][kNf], fb[2][kNf];
-#pragma unroll
-        for (int i = 0; i < kNf; ++i) {
-            fa[0][i] = *reinterpret_cast<const u32x4*>(buf + fa_off + i * 32 * kLdsStride);
-            fb[0][i] = *reinterpret_cast<const u32x4*>(buf + fb_off + i * 32 * kLdsStride);
-        }
+        unsigned char* nbuf = lds + ((kb + 1) & 1) * 2 * G::kOp;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int cur = q & 1;
-            if (q < 3) {
 #pragma unroll
-                for (int i = 0; i < kNf; ++i) {
-                    fa[cur ^ 1][i] = *reinterpret_cast<const u32x4*>(
-                        buf + fa_off + i * 32 * kLdsStride + (q + 1) * 16);
-                    fb[cur ^ 1][i] = *reinterpret_cast<const u32x4*>(
-                        buf + fb_off + i * 32 * kLdsStride + (q + 1) * 16);
+            for (int m = 0; m < kMfma; ++m) {
+                const int i = m / kNf, j = m % kNf;
+                if constexpr (BF16) {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, fa[cur][i]), __builtin_bit_cast(bf16x8, fb[cur][j]),
+                        acc[i][j], 0, 0, 0);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                            __uint_as_float(fa[cur][i][e]), __uint_as_float(fb[cur][j][e]), acc[i][j],
+                            0, 0, 0);
                 }
-            }
-            if constexpr (BF16) {
+                // one memory instruction after this MFMA
+                if (q < 3) {
 #pragma unroll
-                for (int i = 0; i < kNf; ++i)
+                    for (int rd = m; rd < 2 * kNf; rd += kMfma) {
+                        const int f = rd % kNf;
+                        const int at = f * 32 * kLdsStride + (q + 1) * 16;
+                        if (rd < kNf)
+                            fa[cur ^ 1][f] = *reinterpret_cast<const u32x4*>(buf + fa_off + at);
+                        else
+                            fb[cur ^ 1][f] = *reinterpret_cast<const u32x4*>(buf + fb_off + at);
+                    }
+                }
+                if (q == 0) {
+                    // 2*kL loads spread over the kMfma MFMAs of step 0
 #pragma unroll
-                    for (int j = 0; j < kNf; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8, fa[cur][i]),
-                            __builtin_bit_cast(bf16x8, fb[cur][j]), acc[i][j], 0, 0, 0);
-            } else {
+                    for (int l = m; l < 2 * kL; l += kMfma) {
+                        if (l < kL)
+                            pa[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep + k0);
+                        else
+                            pb[l - kL] = *reinterpret_cast<const u32x4*>(gq + (l - kL) * rstep + k0);
+                    }
+                }
+                if (q == 3) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-#pragma unroll
-                    for (int i = 0; i < kNf; ++i)
-#pragma unroll
-                        for (int j = 0; j < kNf; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                                __uint_as_float(fa[cur][i][e]), __uint_as_float(fb[cur][j][e]),
-                                acc[i][j], 0, 0, 0);
-            }
-        }
-        if (more) {
-            unsigned char* nb = lds + ((kb + 1) & 1) * 2 * G::kOp;
-#pragma unroll
-            for (int l = 0; l < kL; ++l) {
-                *reinterpret_cast<u32x4*>(nb + lds_st + l * 32 * kLdsStride) = pa[l];
-                *reinterpret_cast<u32x4*>(nb + G::kOp + lds_st + l * 32 * kLdsStride) = pb[l];
+                    for (int l = m; l < 2 * kL; l += kMfma) {
+                        if (l < kL)
+                            *reinterpret_cast<u32x4*>(nbuf + lds_st + l * 32 * kLdsStride) = pa[l];
+                        else
+                            *reinterpret_cast<u32x4*>(nbuf + G::kOp + lds_st +
+                                                      (l - kL) * 32 * kLdsStride) = pb[l - kL];
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         __syncthreads();
+        // fragments of step 0 of the next block
+#pragma unroll
+        for (int i = 0; i < kNf; ++i) {
+            fa[0][i] = *reinterpret_cast<const u32x4*>(nbuf + fa_off + i * 32 * kLdsStride);
+            fb[0][i] = *reinterpret_cast<const u32x4*>(nbuf + fb_off + i * 32 * kLdsStride);
+        }
     }
 
     // Epilogue.  Lane (lr, hk) of fragment (i, j) holds, for g = 0..3, the
@@ -419,8 +439,9 @@ hipError_t launch_newton_schulz(const PlanView& p, void* ws, float* o, int ns_st
         for (int stage = kStageA; stage <= kStageX; ++stage) {
             for (int c = 0; c < p.n_classes; ++c) {
                 const TileClassDev& tc = p.classes[c];
-                const int count = stage == kStageX ? tc.n_full : tc.n_sym;
-                a.tiles = stage == kStageX ? tc.full : tc.sym;
+                const int count = stage == kStageX ? tc.n_full
+                                  : stage == kStageA ? tc.n_sym_a : tc.n_sym_b;
+                a.tiles = stage == kStageX ? tc.full : stage == kStageA ? tc.sym_a : tc.sym_b;
                 const hipError_t e = bf16 ? launch_class<true>(tc.tile, stage, count, a, s)
                                           : launch_class<false>(tc.tile, stage, count, a, s);
                 if (e != hipSuccess) return e;

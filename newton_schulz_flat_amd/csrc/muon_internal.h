@@ -81,13 +81,15 @@ struct WsLayout {
     size_t total;
 };
 
-// Tiles of one GEMM tile size: symmetric (ti <= tj) and full rp x cp grids.
+// Tiles of one GEMM tile size: the upper triangle (ti <= tj) of rp x rp for
+// stages A and B (the same tiles, balanced for each stage's contraction
+// length), and the full rp x cp grid for stage X.  Device pointers.
 struct TileClassDev {
     int tile;
-    int n_sym;
-    int n_full;
-    const GemmTile* sym;   // device
-    const GemmTile* full;  // device
+    int n_sym_a, n_sym_b, n_full;
+    const GemmTile* sym_a;
+    const GemmTile* sym_b;
+    const GemmTile* full;
 };
 
 // A launch plan for one descriptor set, device and GEMM mode.

@@ -120,19 +120,40 @@ double ns_cost(const MatInfo& m) {
     return 3.0 * r * r * c + r * r * r;
 }
 
-// Lay a logical tile list out so that XCD x (workgroups x, x+8, x+16, ...)
-// receives the x-th contiguous run of the list.  Unused slots get mat = -1.
-std::vector<GemmTile> xcd_interleave(const std::vector<GemmTile>& logical) {
-    const size_t count = logical.size();
-    const size_t per = (count + kXcds - 1) / kXcds;
-    std::vector<GemmTile> out(per * kXcds, GemmTile{-1, 0, 0, 0});
-    for (size_t b = 0; b < out.size(); ++b) {
-        const size_t xcd = b % kXcds, idx = b / kXcds;
-        const size_t src = xcd * per + idx;
-        if (src < count) out[b] = logical[src];
+// Tile table layout.  The hardware hands workgroup b to XCD b % 8, and each
+// XCD has its own L2.  Tiles are cut into chunks of neighbours (tiles of one
+// matrix that share operand panels), chunks are dealt to the XCD with the
+// least work so far in decreasing order of cost (longest-processing-time
+// first), and XCD x's k-th tile is placed at index 8 k + x.  Slots past an
+// XCD's last tile hold mat = -1 (the workgroup exits at once).
+struct Chunk {
+    std::vector<GemmTile> tiles;
+    double cost;
+};
+
+std::vector<GemmTile> balance_over_xcds(std::vector<Chunk> chunks) {
+    std::stable_sort(chunks.begin(), chunks.end(),
+                     [](const Chunk& a, const Chunk& b) { return a.cost > b.cost; });
+    std::vector<std::vector<GemmTile>> per(kXcds);
+    double load[kXcds] = {0};
+    for (const Chunk& c : chunks) {
+        int best = 0;
+        for (int x = 1; x < kXcds; ++x)
+            if (load[x] < load[best]) best = x;
+        load[best] += c.cost;
+        per[best].insert(per[best].end(), c.tiles.begin(), c.tiles.end());
     }
+    size_t rows = 0;
+    for (const auto& v : per) rows = std::max(rows, v.size());
+    std::vector<GemmTile> out(rows * kXcds, GemmTile{-1, 0, 0, 0});
+    for (int x = 0; x < kXcds; ++x)
+        for (size_t k = 0; k < per[x].size(); ++k) out[k * kXcds + size_t(x)] = per[x][k];
     return out;
 }
+
+// Per-tile cost in K blocks of 64, plus a fixed share for the epilogue.
+constexpr double kEpilogueBlocks = 8.0;
+constexpr size_t kChunkTiles = 8;
 
 }  // namespace
 
@@ -145,7 +166,7 @@ struct PlanStore {
     PlanView view{};
     std::vector<MatInfo> mats;
     std::vector<int32_t> chunk_prefix, cast_prefix;
-    std::vector<GemmTile> sym[3], full[3];
+    std::vector<GemmTile> sym_a[3], sym_b[3], full[3];
     std::vector<unsigned char> host_blob;  // staging copy of the device tables
     void* dev = nullptr;
     int device = -1;
@@ -181,19 +202,39 @@ std::shared_ptr<PlanStore> build_plan(const muon_matrix_desc_t* d, int64_t n, in
         if (ca != cb) return ca > cb;
         return p->mats[size_t(a)].off < p->mats[size_t(b)].off;
     });
-    std::vector<GemmTile> sym_logical[3], full_logical[3];
+    std::vector<Chunk> sym_a_chunks[3], sym_b_chunks[3], full_chunks[3];
+    auto add_chunks = [](std::vector<Chunk>& dst, const std::vector<GemmTile>& tiles,
+                         double tile_cost) {
+        for (size_t b = 0; b < tiles.size(); b += kChunkTiles) {
+            Chunk c;
+            c.tiles.assign(tiles.begin() + b, tiles.begin() + std::min(tiles.size(), b + kChunkTiles));
+            c.cost = tile_cost * double(c.tiles.size());
+            dst.push_back(std::move(c));
+        }
+    };
     for (int32_t mi : order) {
         const MatInfo& m = p->mats[size_t(mi)];
         const int cls = class_index(m.tile);
         const int nr = m.rp / m.tile, nc = m.cp / m.tile;
+        // symmetric stages: upper-triangle tiles band by band (a chunk shares row panels)
+        std::vector<GemmTile> sym;
         for (int ti = 0; ti < nr; ++ti)
-            for (int tj = ti; tj < nr; ++tj) sym_logical[cls].push_back({mi, ti, tj, 0});
-        for (int ti = 0; ti < nr; ++ti)
-            for (int tj = 0; tj < nc; ++tj) full_logical[cls].push_back({mi, ti, tj, 0});
+            for (int tj = ti; tj < nr; ++tj) sym.push_back({mi, ti, tj, 0});
+        // full grid: bands of up to 4 tile rows walked column by column (a chunk of 8
+        // covers 4 x 2 tiles: 4 row panels of B and 2 panels of X^T)
+        std::vector<GemmTile> full;
+        for (int t0 = 0; t0 < nr; t0 += 4)
+            for (int tj = 0; tj < nc; ++tj)
+                for (int ti = t0; ti < std::min(nr, t0 + 4); ++ti) full.push_back({mi, ti, tj, 0});
+        // stage A contracts over cp, stages B and X over rp
+        add_chunks(sym_a_chunks[cls], sym, double(m.cp) / 64.0 + kEpilogueBlocks);
+        add_chunks(sym_b_chunks[cls], sym, double(m.rp) / 64.0 + kEpilogueBlocks);
+        add_chunks(full_chunks[cls], full, double(m.rp) / 64.0 + kEpilogueBlocks);
     }
     for (int c = 0; c < 3; ++c) {
-        p->sym[c] = xcd_interleave(sym_logical[c]);
-        p->full[c] = xcd_interleave(full_logical[c]);
+        p->sym_a[c] = balance_over_xcds(std::move(sym_a_chunks[c]));
+        p->sym_b[c] = balance_over_xcds(std::move(sym_b_chunks[c]));
+        p->full[c] = balance_over_xcds(std::move(full_chunks[c]));
     }
 
     // One device blob: mats | chunk prefix | cast prefix | tile tables.
@@ -206,9 +247,10 @@ std::shared_ptr<PlanStore> build_plan(const muon_matrix_desc_t* d, int64_t n, in
     const size_t o_mats = reserve(p->mats.size() * sizeof(MatInfo));
     const size_t o_cp = reserve(p->chunk_prefix.size() * 4);
     const size_t o_kp = reserve(p->cast_prefix.size() * 4);
-    size_t o_sym[3], o_full[3];
+    size_t o_sym_a[3], o_sym_b[3], o_full[3];
     for (int c = 0; c < 3; ++c) {
-        o_sym[c] = reserve(p->sym[c].size() * sizeof(GemmTile));
+        o_sym_a[c] = reserve(p->sym_a[c].size() * sizeof(GemmTile));
+        o_sym_b[c] = reserve(p->sym_b[c].size() * sizeof(GemmTile));
         o_full[c] = reserve(p->full[c].size() * sizeof(GemmTile));
     }
     const size_t blob = std::max<size_t>(at, 256);
@@ -220,7 +262,8 @@ std::shared_ptr<PlanStore> build_plan(const muon_matrix_desc_t* d, int64_t n, in
     put(o_cp, p->chunk_prefix.data(), p->chunk_prefix.size() * 4);
     put(o_kp, p->cast_prefix.data(), p->cast_prefix.size() * 4);
     for (int c = 0; c < 3; ++c) {
-        put(o_sym[c], p->sym[c].data(), p->sym[c].size() * sizeof(GemmTile));
+        put(o_sym_a[c], p->sym_a[c].data(), p->sym_a[c].size() * sizeof(GemmTile));
+        put(o_sym_b[c], p->sym_b[c].data(), p->sym_b[c].size() * sizeof(GemmTile));
         put(o_full[c], p->full[c].data(), p->full[c].size() * sizeof(GemmTile));
     }
     hipError_t e = hipMalloc(&p->dev, blob);
@@ -254,9 +297,11 @@ std::shared_ptr<PlanStore> build_plan(const muon_matrix_desc_t* d, int64_t n, in
     const int tiles[3] = {256, 128, 64};
     for (int c = 0; c < 3; ++c) {
         v.classes[c].tile = tiles[c];
-        v.classes[c].n_sym = int(p->sym[c].size());
+        v.classes[c].n_sym_a = int(p->sym_a[c].size());
+        v.classes[c].n_sym_b = int(p->sym_b[c].size());
         v.classes[c].n_full = int(p->full[c].size());
-        v.classes[c].sym = reinterpret_cast<const GemmTile*>(base + o_sym[c]);
+        v.classes[c].sym_a = reinterpret_cast<const GemmTile*>(base + o_sym_a[c]);
+        v.classes[c].sym_b = reinterpret_cast<const GemmTile*>(base + o_sym_b[c]);
         v.classes[c].full = reinterpret_cast<const GemmTile*>(base + o_full[c]);
     }
     return p;
