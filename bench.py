@@ -58,6 +58,27 @@ def elementwise_bytes(wl):
             "apply": 4 * n + 2 * wb * n}  # O read, W read + write
 
 
+KERNEL_SOURCES = ("k_ns_gemm.hip", "k_elementwise.hip", "k_norm_cast.hip")
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch (read + written) that profiler counters recorded for
+    this kernel on this workload, if the kernel sources are unchanged since;
+    otherwise None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
+    try:
+        rec = json.load(open(path))
+        for f in KERNEL_SOURCES:
+            src = os.path.join(ROOT, "newton_schulz_flat_amd", "csrc", f)
+            if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["sources_sha256"][f]:
+                return None
+        b = rec["per_launch_bytes"][kernel]
+        return b["read"] + b["written"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(wl, budget_s=20.0):
     """Oracle (fp64 NumPy) step time on a bounded sample, scaled to the workload."""
     import numpy as np
@@ -180,7 +201,7 @@ def main():
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "work_per_launch": work,
                 "avg_launch_ms": avg_s * 1e3}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = recorded_traffic(name, "llama_layer" if wl.name == "llama" else wl.name)
 
     per_kernel = {k: {"ms_per_step": v[0] / args.steps, "launches_per_step": v[1] / args.steps}
                   for k, v in sorted(kernels.items())}
