@@ -302,28 +302,111 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(NsArgs args) {
         const TE* opnd = nullptr;  // epilogue operand, read column-oriented
         if (STAGE == kStageB) opnd = static_cast<const TE*>(args.ga) + mt.g_off;
         if (STAGE == kStageX) opnd = static_cast<const TE*>(args.xt_cur) + mt.x_off;
+        if constexpr (BF16) {
+            // bfloat16 outputs go through LDS so that every global store writes
+            // 16 contiguous bytes per lane along an output row.  Each wave stages its
+            // own kWt x kWt sub-tile (rows padded by 16 bytes) in a private region:
+            // first in the column-oriented layout (for out_t), then in the
+            // row-oriented layout (for out_n, via the quad exchange).  The values
+            // are rounded to bfloat16 once and kept packed in registers between
+            // the two passes.  The main loop ended with a barrier, so LDS is free.
+            constexpr int kW = G::kWt;
+            constexpr int kStride = kW * 2 + 16;  // bytes per staged row
+            constexpr int kChunks = kW * kW * 2 / 16 / 64;  // 16-byte chunks per lane
+            unsigned char* wl = lds + wave * (kW * kStride);
+            uint32_t pk[kNf][kNf][4][2];
 #pragma unroll
-        for (int i = 0; i < kNf; ++i) {
+            for (int i = 0; i < kNf; ++i) {
 #pragma unroll
-            for (int j = 0; j < kNf; ++j) {
+                for (int j = 0; j < kNf; ++j) {
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int gi = row0 + i * 32 + g * 8;
-                    const int gj = col0 + j * 32;
-                    float v[4];
+                    for (int g = 0; g < 4; ++g) {
+                        const int gi = row0 + i * 32 + g * 8;
+                        const int gj = col0 + j * 32;
+                        float v[4];
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) v[t] = acc[i][j][g * 4 + t];
-                    if (STAGE != kStageA) {
-                        float ov[4];
-                        load4(opnd + int64_t(gj) * rp + gi, ov);
+                        for (int t = 0; t < 4; ++t) v[t] = acc[i][j][g * 4 + t];
+                        if (STAGE != kStageA) {
+                            float ov[4];
+                            load4(opnd + int64_t(gj) * rp + gi, ov);
 #pragma unroll
-                        for (int t = 0; t < 4; ++t)
-                            v[t] = STAGE == kStageB ? cb * ov[t] + cc * v[t] : ca * ov[t] + v[t];
+                            for (int t = 0; t < 4; ++t)
+                                v[t] = STAGE == kStageB ? cb * ov[t] + cc * v[t] : ca * ov[t] + v[t];
+                        }
+                        pk[i][j][g][0] = uint32_t(bf16_rne(v[0])) | (uint32_t(bf16_rne(v[1])) << 16);
+                        pk[i][j][g][1] = uint32_t(bf16_rne(v[2])) | (uint32_t(bf16_rne(v[3])) << 16);
                     }
-                    if (write_t) store4(out_t + int64_t(gj) * ld_t + gi, v);
-                    float w[4];
-                    quad_transpose(v, w, s4);
-                    store4(out_n + int64_t(gi + s4) * ld_n + (gj - s4), w);
+                }
+            }
+            // staged row r of the sub-tile -> global row base_r + r, columns base_c + ...
+            auto drain = [&](TE* out, int ld, int base_r, int base_c) {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+                for (int t = 0; t < kChunks; ++t) {
+                    const int ch = t * 64 + lane;
+                    const int r = ch / (kW / 8), c16 = ch % (kW / 8);
+                    const u32x4 val = *reinterpret_cast<const u32x4*>(wl + r * kStride + c16 * 16);
+                    *reinterpret_cast<u32x4*>(out + int64_t(base_r + r) * ld + base_c + c16 * 8) = val;
+                }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            };
+            if (write_t) {
+                // column-oriented: staged row = output column j*32 + lr, 4 rows per lane
+#pragma unroll
+                for (int i = 0; i < kNf; ++i)
+#pragma unroll
+                    for (int j = 0; j < kNf; ++j)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const int sr = j * 32 + lr, sc = i * 32 + g * 8 + hk * 4;
+                            *reinterpret_cast<uint2*>(wl + sr * kStride + sc * 2) =
+                                make_uint2(pk[i][j][g][0], pk[i][j][g][1]);
+                        }
+                drain(out_t, ld_t, tj * TILE + wn * kW, ti * TILE + wm * kW);
+            }
+            // row-oriented: after the quad exchange lane s holds row (.. + s), columns c - s ..
+#pragma unroll
+            for (int i = 0; i < kNf; ++i)
+#pragma unroll
+                for (int j = 0; j < kNf; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        float v[4], w[4];
+                        v[0] = __uint_as_float(pk[i][j][g][0] << 16);
+                        v[1] = __uint_as_float(pk[i][j][g][0] & 0xffff0000u);
+                        v[2] = __uint_as_float(pk[i][j][g][1] << 16);
+                        v[3] = __uint_as_float(pk[i][j][g][1] & 0xffff0000u);
+                        quad_transpose(v, w, s4);
+                        const uint32_t lo = (__float_as_uint(w[0]) >> 16) | (__float_as_uint(w[1]) & 0xffff0000u);
+                        const uint32_t hi = (__float_as_uint(w[2]) >> 16) | (__float_as_uint(w[3]) & 0xffff0000u);
+                        const int sr = i * 32 + g * 8 + hk * 4 + s4, sc = j * 32 + lr - s4;
+                        *reinterpret_cast<uint2*>(wl + sr * kStride + sc * 2) = make_uint2(lo, hi);
+                    }
+            drain(out_n, ld_n, ti * TILE + wm * kW, tj * TILE + wn * kW);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kNf; ++i) {
+#pragma unroll
+                for (int j = 0; j < kNf; ++j) {
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int gi = row0 + i * 32 + g * 8;
+                        const int gj = col0 + j * 32;
+                        float v[4];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) v[t] = acc[i][j][g * 4 + t];
+                        if (STAGE != kStageA) {
+                            float ov[4];
+                            load4(opnd + int64_t(gj) * rp + gi, ov);
+#pragma unroll
+                            for (int t = 0; t < 4; ++t)
+                                v[t] = STAGE == kStageB ? cb * ov[t] + cc * v[t] : ca * ov[t] + v[t];
+                        }
+                        if (write_t) store4(out_t + int64_t(gj) * ld_t + gi, v);
+                        float w[4];
+                        quad_transpose(v, w, s4);
+                        store4(out_n + int64_t(gi + s4) * ld_n + (gj - s4), w);
+                    }
                 }
             }
         }

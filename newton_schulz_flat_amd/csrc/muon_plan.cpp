@@ -121,8 +121,9 @@ double ns_cost(const MatInfo& m) {
 }
 
 // Tile table layout.  The hardware hands workgroup b to XCD b % 8, and each
-// XCD has its own L2.  Tiles are cut into chunks of neighbours (tiles of one
-// matrix that share operand panels), chunks are dealt to the XCD with the
+// XCD (32 CUs) has its own L2.  Tiles are cut into chunks of 32 neighbours
+// (tiles of one matrix that share operand panels, so the 32 tiles an XCD runs
+// at once read few distinct panels), chunks are dealt to the XCD with the
 // least work so far in decreasing order of cost (longest-processing-time
 // first), and XCD x's k-th tile is placed at index 8 k + x.  Slots past an
 // XCD's last tile hold mat = -1 (the workgroup exits at once).
@@ -153,7 +154,12 @@ std::vector<GemmTile> balance_over_xcds(std::vector<Chunk> chunks) {
 
 // Per-tile cost in K blocks of 64, plus a fixed share for the epilogue.
 constexpr double kEpilogueBlocks = 8.0;
-constexpr size_t kChunkTiles = 8;
+// Chunk size: up to 32 neighbours (one per CU of an XCD), but small enough
+// that every XCD receives about eight chunks to balance.
+size_t chunk_tiles(size_t total) {
+    const size_t c = total / (kXcds * 8);
+    return std::max<size_t>(4, std::min<size_t>(32, c / 4 * 4));
+}
 
 }  // namespace
 
@@ -202,39 +208,52 @@ std::shared_ptr<PlanStore> build_plan(const muon_matrix_desc_t* d, int64_t n, in
         if (ca != cb) return ca > cb;
         return p->mats[size_t(a)].off < p->mats[size_t(b)].off;
     });
-    std::vector<Chunk> sym_a_chunks[3], sym_b_chunks[3], full_chunks[3];
-    auto add_chunks = [](std::vector<Chunk>& dst, const std::vector<GemmTile>& tiles,
-                         double tile_cost) {
-        for (size_t b = 0; b < tiles.size(); b += kChunkTiles) {
-            Chunk c;
-            c.tiles.assign(tiles.begin() + b, tiles.begin() + std::min(tiles.size(), b + kChunkTiles));
-            c.cost = tile_cost * double(c.tiles.size());
-            dst.push_back(std::move(c));
-        }
+    // tiles of each matrix in locality order, with their cost in K blocks
+    struct Run {
+        std::vector<GemmTile> tiles;
+        double tile_cost;
+    };
+    std::vector<Run> sym_a_runs[3], sym_b_runs[3], full_runs[3];
+    auto chunk_all = [](const std::vector<Run>& runs) {
+        size_t total = 0;
+        for (const Run& r : runs) total += r.tiles.size();
+        const size_t per = chunk_tiles(total);
+        std::vector<Chunk> out;
+        for (const Run& r : runs)
+            for (size_t b = 0; b < r.tiles.size(); b += per) {
+                Chunk c;
+                c.tiles.assign(r.tiles.begin() + b, r.tiles.begin() + std::min(r.tiles.size(), b + per));
+                c.cost = r.tile_cost * double(c.tiles.size());
+                out.push_back(std::move(c));
+            }
+        return out;
     };
     for (int32_t mi : order) {
         const MatInfo& m = p->mats[size_t(mi)];
         const int cls = class_index(m.tile);
         const int nr = m.rp / m.tile, nc = m.cp / m.tile;
-        // symmetric stages: upper-triangle tiles band by band (a chunk shares row panels)
+        // symmetric stages: bands of 8 tile rows walked column by column over the
+        // upper triangle, so a chunk of 32 neighbours touches few row panels
         std::vector<GemmTile> sym;
-        for (int ti = 0; ti < nr; ++ti)
-            for (int tj = ti; tj < nr; ++tj) sym.push_back({mi, ti, tj, 0});
-        // full grid: bands of up to 4 tile rows walked column by column (a chunk of 8
-        // covers 4 x 2 tiles: 4 row panels of B and 2 panels of X^T)
+        for (int t0 = 0; t0 < nr; t0 += 8)
+            for (int tj = t0; tj < nr; ++tj)
+                for (int ti = t0; ti < std::min(nr, t0 + 8); ++ti)
+                    if (ti <= tj) sym.push_back({mi, ti, tj, 0});
+        // full grid: bands of 8 tile rows walked column by column; a chunk of 32
+        // covers 8 x 4 tiles (8 row panels of B and 4 row panels of X^T)
         std::vector<GemmTile> full;
-        for (int t0 = 0; t0 < nr; t0 += 4)
+        for (int t0 = 0; t0 < nr; t0 += 8)
             for (int tj = 0; tj < nc; ++tj)
-                for (int ti = t0; ti < std::min(nr, t0 + 4); ++ti) full.push_back({mi, ti, tj, 0});
+                for (int ti = t0; ti < std::min(nr, t0 + 8); ++ti) full.push_back({mi, ti, tj, 0});
         // stage A contracts over cp, stages B and X over rp
-        add_chunks(sym_a_chunks[cls], sym, double(m.cp) / 64.0 + kEpilogueBlocks);
-        add_chunks(sym_b_chunks[cls], sym, double(m.rp) / 64.0 + kEpilogueBlocks);
-        add_chunks(full_chunks[cls], full, double(m.rp) / 64.0 + kEpilogueBlocks);
+        sym_a_runs[cls].push_back({sym, double(m.cp) / 64.0 + kEpilogueBlocks});
+        sym_b_runs[cls].push_back({sym, double(m.rp) / 64.0 + kEpilogueBlocks});
+        full_runs[cls].push_back({std::move(full), double(m.rp) / 64.0 + kEpilogueBlocks});
     }
     for (int c = 0; c < 3; ++c) {
-        p->sym_a[c] = balance_over_xcds(std::move(sym_a_chunks[c]));
-        p->sym_b[c] = balance_over_xcds(std::move(sym_b_chunks[c]));
-        p->full[c] = balance_over_xcds(std::move(full_chunks[c]));
+        p->sym_a[c] = balance_over_xcds(chunk_all(sym_a_runs[c]));
+        p->sym_b[c] = balance_over_xcds(chunk_all(sym_b_runs[c]));
+        p->full[c] = balance_over_xcds(chunk_all(full_runs[c]));
     }
 
     // One device blob: mats | chunk prefix | cast prefix | tile tables.
