@@ -21,8 +21,9 @@
 // ping-pong buffer; on the last iteration it writes O = fl(s * X) in the
 // matrix's original orientation instead.
 //
-// Workgroup: 256 threads = 4 waves in a 2 x 2 grid over a TILE x TILE output
-// tile; each wave owns (TILE/2)^2 outputs as 32 x 32 MFMA fragments.  K is
+// Workgroup: 4 waves in a 2 x 2 grid over a TILE x TILE output tile (8 waves,
+// 2 x 4, for the 256 x 256 bf16 tile); each wave owns its block of outputs as
+// 32 x 32 MFMA fragments.  K is
 // consumed in blocks of 128 bytes per row (64 bf16 / 32 float32), staged
 // through double-buffered LDS with rows padded to 144 bytes so that the 16-byte
 // fragment reads of 8 consecutive rows hit distinct banks.  One grouped launch
@@ -56,12 +57,20 @@ struct NsArgs {
 constexpr int kRowBytes = 128;  // K block: bytes of one operand row
 constexpr int kLdsStride = 144;  // padded LDS row
 
-template <int TILE>
-struct TileGeo {
-    static constexpr int kOp = TILE * kLdsStride;            // bytes of one operand tile
-    static constexpr int kWt = TILE / 2;                     // wave tile side
-    static constexpr int kNf = kWt / 32;                     // fragments per wave side
-    static constexpr int kLoads = TILE * (kRowBytes / 16) / 256;  // 16-byte loads / thread / operand
+// Workgroup geometry.  The 256 x 256 bf16 tile uses 8 waves (two per SIMD,
+// each wave 128 x 64 outputs): a wave waiting on memory leaves the matrix
+// pipe to its partner, and the two-per-SIMD LDS read rate is about twice
+// the one-per-SIMD rate.  Smaller tiles and float32 use 4 waves (2 x 2).
+template <int TILE, bool BF16>
+struct Geo {
+    static constexpr int kWaves = (TILE == 256 && BF16) ? 8 : 4;
+    static constexpr int kThreads = kWaves * 64;
+    static constexpr int kOp = TILE * kLdsStride;       // bytes of one staged operand tile
+    static constexpr int kWm = TILE / 2;                 // wave tile rows
+    static constexpr int kWn = TILE / (kWaves / 2);      // wave tile columns
+    static constexpr int kMi = kWm / 32, kNj = kWn / 32;  // 32 x 32 fragments per wave
+    static constexpr int kRowsPerPass = kThreads / 8;    // operand rows one load pass covers
+    static constexpr int kLoads = TILE / kRowsPerPass;   // 16-byte loads per thread per operand
 };
 
 __device__ __forceinline__ float load_e(const float* p) { return *p; }
@@ -120,12 +129,12 @@ __device__ __forceinline__ void quad_transpose(const float v[4], float w[4], int
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <int TILE, bool BF16, int STAGE>
-__global__ __launch_bounds__(256) void ns_gemm_kernel(NsArgs args) {
+__global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(NsArgs args) {
     using TE = std::conditional_t<BF16, uint16_t, float>;
-    using G = TileGeo<TILE>;
+    using G = Geo<TILE, BF16>;
     constexpr int kEs = BF16 ? 2 : 4;
     constexpr int kBk = kRowBytes / kEs;  // K elements per block
-    constexpr int kNf = G::kNf;
+    constexpr int kMi = G::kMi, kNj = G::kNj;
     constexpr int kL = G::kLoads;
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * 2 * G::kOp];
 
@@ -158,25 +167,26 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(NsArgs args) {
     }
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave & 1, wn = wave >> 1;
     const int lr = lane & 31, hk = lane >> 5;
 
     // Global -> LDS staging: thread tid moves 16-byte chunk (tid & 7) of rows
-    // (tid >> 3) + 32 l, l = 0..kL-1, of each operand's K block.
+    // (tid >> 3) + l * kRowsPerPass, l = 0..kL-1, of each operand's K block.
     const int lrow = tid >> 3, lchunk = tid & 7;
     const TE* gp = P + int64_t(lrow) * ld + lchunk * (16 / kEs);
     const TE* gq = Q + int64_t(lrow) * ld + lchunk * (16 / kEs);
-    const int64_t rstep = int64_t(32) * ld;
+    const int64_t rstep = int64_t(G::kRowsPerPass) * ld;
     const int lds_st = lrow * kLdsStride + lchunk * 16;
+    constexpr int kLdsPass = G::kRowsPerPass * kLdsStride;
     // Fragment reads: row lr of each 32-row fragment, bytes [hk*64, hk*64 + 64).
-    const int fa_off = (wm * G::kWt + lr) * kLdsStride + hk * 64;
-    const int fb_off = G::kOp + (wn * G::kWt + lr) * kLdsStride + hk * 64;
+    const int fa_off = (wm * G::kWm + lr) * kLdsStride + hk * 64;
+    const int fb_off = G::kOp + (wn * G::kWn + lr) * kLdsStride + hk * 64;
 
-    f32x16 acc[kNf][kNf];
+    f32x16 acc[kMi][kNj];
 #pragma unroll
-    for (int i = 0; i < kNf; ++i)
+    for (int i = 0; i < kMi; ++i)
 #pragma unroll
-        for (int j = 0; j < kNf; ++j)
+        for (int j = 0; j < kNj; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
@@ -188,27 +198,28 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(NsArgs args) {
     }
 #pragma unroll
     for (int l = 0; l < kL; ++l) {
-        *reinterpret_cast<u32x4*>(lds + lds_st + l * 32 * kLdsStride) = pa[l];
-        *reinterpret_cast<u32x4*>(lds + G::kOp + lds_st + l * 32 * kLdsStride) = pb[l];
+        *reinterpret_cast<u32x4*>(lds + lds_st + l * kLdsPass) = pa[l];
+        *reinterpret_cast<u32x4*>(lds + G::kOp + lds_st + l * kLdsPass) = pb[l];
     }
     __syncthreads();
 
     // Main loop.  One K block is a single basic block whose instruction order
-    // is fixed with scheduling barriers: each MFMA is followed by at most one
-    // memory instruction, so the matrix pipe keeps issuing while
-    //   q = 0: the 2*kL global loads of the block after next are issued,
+    // is fixed with scheduling barriers: each MFMA is followed by at most a few
+    // memory instructions, so the matrix pipe keeps issuing while
+    //   q = 0: the 2*kL global loads of the next block are issued,
     //   q < 3: the fragments of step q+1 are read from LDS (double-buffered
     //          registers),
     //   q = 3: the prefetched block is written to the other LDS buffer.
     // The last block reloads itself (a valid, unused copy) to stay branch free.
     const int nkb = K / kBk;
-    constexpr int kMfma = kNf * kNf;  // MFMAs per step q (per K sub-step for bf16)
-    u32x4 fa[2][kNf], fb[2][kNf];
+    constexpr int kMfma = kMi * kNj;  // MFMAs per step q (per K sub-step for bf16)
+    u32x4 fa[2][kMi], fb[2][kNj];
 #pragma unroll
-    for (int i = 0; i < kNf; ++i) {
+    for (int i = 0; i < kMi; ++i)
         fa[0][i] = *reinterpret_cast<const u32x4*>(lds + fa_off + i * 32 * kLdsStride);
-        fb[0][i] = *reinterpret_cast<const u32x4*>(lds + fb_off + i * 32 * kLdsStride);
-    }
+#pragma unroll
+    for (int j = 0; j < kNj; ++j)
+        fb[0][j] = *reinterpret_cast<const u32x4*>(lds + fb_off + j * 32 * kLdsStride);
     for (int kb = 0; kb < nkb; ++kb) {
         const int64_t k0 = int64_t(kb + 1 < nkb ? kb + 1 : kb) * kBk;
         const unsigned char* buf = lds + (kb & 1) * 2 * G::kOp;
@@ -218,7 +229,7 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(NsArgs args) {
             const int cur = q & 1;
 #pragma unroll
             for (int m = 0; m < kMfma; ++m) {
-                const int i = m / kNf, j = m % kNf;
+                const int i = m / kNj, j = m % kNj;
                 if constexpr (BF16) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         __builtin_bit_cast(bf16x8, fa[cur][i]), __builtin_bit_cast(bf16x8, fb[cur][j]),
@@ -230,20 +241,19 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(NsArgs args) {
                             __uint_as_float(fa[cur][i][e]), __uint_as_float(fb[cur][j][e]), acc[i][j],
                             0, 0, 0);
                 }
-                // one memory instruction after this MFMA
                 if (q < 3) {
 #pragma unroll
-                    for (int rd = m; rd < 2 * kNf; rd += kMfma) {
-                        const int f = rd % kNf;
-                        const int at = f * 32 * kLdsStride + (q + 1) * 16;
-                        if (rd < kNf)
-                            fa[cur ^ 1][f] = *reinterpret_cast<const u32x4*>(buf + fa_off + at);
+                    for (int rd = m; rd < kMi + kNj; rd += kMfma) {
+                        const int at = (q + 1) * 16;
+                        if (rd < kMi)
+                            fa[cur ^ 1][rd] = *reinterpret_cast<const u32x4*>(
+                                buf + fa_off + rd * 32 * kLdsStride + at);
                         else
-                            fb[cur ^ 1][f] = *reinterpret_cast<const u32x4*>(buf + fb_off + at);
+                            fb[cur ^ 1][rd - kMi] = *reinterpret_cast<const u32x4*>(
+                                buf + fb_off + (rd - kMi) * 32 * kLdsStride + at);
                     }
                 }
                 if (q == 0) {
-                    // 2*kL loads spread over the kMfma MFMAs of step 0
 #pragma unroll
                     for (int l = m; l < 2 * kL; l += kMfma) {
                         if (l < kL)
@@ -256,10 +266,10 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(NsArgs args) {
 #pragma unroll
                     for (int l = m; l < 2 * kL; l += kMfma) {
                         if (l < kL)
-                            *reinterpret_cast<u32x4*>(nbuf + lds_st + l * 32 * kLdsStride) = pa[l];
+                            *reinterpret_cast<u32x4*>(nbuf + lds_st + l * kLdsPass) = pa[l];
                         else
-                            *reinterpret_cast<u32x4*>(nbuf + G::kOp + lds_st +
-                                                      (l - kL) * 32 * kLdsStride) = pb[l - kL];
+                            *reinterpret_cast<u32x4*>(nbuf + G::kOp + lds_st + (l - kL) * kLdsPass) =
+                                pb[l - kL];
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -268,20 +278,21 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(NsArgs args) {
         __syncthreads();
         // fragments of step 0 of the next block
 #pragma unroll
-        for (int i = 0; i < kNf; ++i) {
+        for (int i = 0; i < kMi; ++i)
             fa[0][i] = *reinterpret_cast<const u32x4*>(nbuf + fa_off + i * 32 * kLdsStride);
-            fb[0][i] = *reinterpret_cast<const u32x4*>(nbuf + fb_off + i * 32 * kLdsStride);
-        }
+#pragma unroll
+        for (int j = 0; j < kNj; ++j)
+            fb[0][j] = *reinterpret_cast<const u32x4*>(nbuf + fb_off + j * 32 * kLdsStride);
     }
 
     // Epilogue.  Lane (lr, hk) of fragment (i, j) holds, for g = 0..3, the
-    // outputs at rows gi + 0..3 (gi = tile row + i*32 + g*8 + hk*4) of column gj.
+    // outputs at rows gi + 0..3 (gi = wave row + i*32 + g*8 + hk*4) of column gj.
     // Column-oriented stores take those 4 values as one vector; row-oriented
     // stores first exchange them across the lane quad so that lane s of the
     // quad holds row gi + s, columns gj - s .. gj - s + 3.
     const int s4 = lr & 3;
-    const int row0 = ti * TILE + wm * G::kWt + hk * 4;
-    const int col0 = tj * TILE + wn * G::kWt + lr;
+    const int row0 = ti * TILE + wm * G::kWm + hk * 4;
+    const int col0 = tj * TILE + wn * G::kWn + lr;
     const float ca = args.ca, cb = args.cb, cc = args.cc;
     if (STAGE != kStageX || !args.last) {
         TE* out_n;  // row-oriented destination, leading dimension ld_n
@@ -305,20 +316,22 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(NsArgs args) {
         if constexpr (BF16) {
             // bfloat16 outputs go through LDS so that every global store writes
             // 16 contiguous bytes per lane along an output row.  Each wave stages its
-            // own kWt x kWt sub-tile (rows padded by 16 bytes) in a private region:
+            // own kWm x kWn sub-tile (rows padded by 16 bytes) in a private region:
             // first in the column-oriented layout (for out_t), then in the
             // row-oriented layout (for out_n, via the quad exchange).  The values
             // are rounded to bfloat16 once and kept packed in registers between
             // the two passes.  The main loop ended with a barrier, so LDS is free.
-            constexpr int kW = G::kWt;
-            constexpr int kStride = kW * 2 + 16;  // bytes per staged row
-            constexpr int kChunks = kW * kW * 2 / 16 / 64;  // 16-byte chunks per lane
-            unsigned char* wl = lds + wave * (kW * kStride);
-            uint32_t pk[kNf][kNf][4][2];
+            constexpr int kWm = G::kWm, kWn = G::kWn;
+            constexpr int kStrideT = kWm * 2 + 16;  // column-oriented: kWn rows of kWm
+            constexpr int kStrideN = kWn * 2 + 16;  // row-oriented: kWm rows of kWn
+            constexpr int kRegion = (kWn * kStrideT > kWm * kStrideN) ? kWn * kStrideT : kWm * kStrideN;
+            static_assert(kRegion * G::kWaves <= 2 * 2 * G::kOp, "epilogue staging exceeds LDS");
+            unsigned char* wl = lds + wave * kRegion;
+            uint32_t pk[kMi][kNj][4][2];
 #pragma unroll
-            for (int i = 0; i < kNf; ++i) {
+            for (int i = 0; i < kMi; ++i) {
 #pragma unroll
-                for (int j = 0; j < kNf; ++j) {
+                for (int j = 0; j < kNj; ++j) {
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const int gi = row0 + i * 32 + g * 8;
@@ -338,37 +351,40 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(NsArgs args) {
                     }
                 }
             }
-            // staged row r of the sub-tile -> global row base_r + r, columns base_c + ...
-            auto drain = [&](TE* out, int ld, int base_r, int base_c) {
+            // staged row r (cols elements each, stride bytes apart) -> global row
+            // base_r + r, columns base_c ..
+            auto drain = [&](TE* out, int ldo, int base_r, int base_c, int cols, int stride,
+                             int rows) {
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-                for (int t = 0; t < kChunks; ++t) {
+                const int cpr = cols / 8;  // 16-byte chunks per staged row
+                const int chunks = rows * cpr / 64;
+                for (int t = 0; t < chunks; ++t) {
                     const int ch = t * 64 + lane;
-                    const int r = ch / (kW / 8), c16 = ch % (kW / 8);
-                    const u32x4 val = *reinterpret_cast<const u32x4*>(wl + r * kStride + c16 * 16);
-                    *reinterpret_cast<u32x4*>(out + int64_t(base_r + r) * ld + base_c + c16 * 8) = val;
+                    const int r = ch / cpr, c16 = ch % cpr;
+                    const u32x4 val = *reinterpret_cast<const u32x4*>(wl + r * stride + c16 * 16);
+                    *reinterpret_cast<u32x4*>(out + int64_t(base_r + r) * ldo + base_c + c16 * 8) = val;
                 }
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             };
             if (write_t) {
                 // column-oriented: staged row = output column j*32 + lr, 4 rows per lane
 #pragma unroll
-                for (int i = 0; i < kNf; ++i)
+                for (int i = 0; i < kMi; ++i)
 #pragma unroll
-                    for (int j = 0; j < kNf; ++j)
+                    for (int j = 0; j < kNj; ++j)
 #pragma unroll
                         for (int g = 0; g < 4; ++g) {
                             const int sr = j * 32 + lr, sc = i * 32 + g * 8 + hk * 4;
-                            *reinterpret_cast<uint2*>(wl + sr * kStride + sc * 2) =
+                            *reinterpret_cast<uint2*>(wl + sr * kStrideT + sc * 2) =
                                 make_uint2(pk[i][j][g][0], pk[i][j][g][1]);
                         }
-                drain(out_t, ld_t, tj * TILE + wn * kW, ti * TILE + wm * kW);
+                drain(out_t, ld_t, tj * TILE + wn * kWn, ti * TILE + wm * kWm, kWm, kStrideT, kWn);
             }
             // row-oriented: after the quad exchange lane s holds row (.. + s), columns c - s ..
 #pragma unroll
-            for (int i = 0; i < kNf; ++i)
+            for (int i = 0; i < kMi; ++i)
 #pragma unroll
-                for (int j = 0; j < kNf; ++j)
+                for (int j = 0; j < kNj; ++j)
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         float v[4], w[4];
@@ -380,14 +396,14 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(NsArgs args) {
                         const uint32_t lo = (__float_as_uint(w[0]) >> 16) | (__float_as_uint(w[1]) & 0xffff0000u);
                         const uint32_t hi = (__float_as_uint(w[2]) >> 16) | (__float_as_uint(w[3]) & 0xffff0000u);
                         const int sr = i * 32 + g * 8 + hk * 4 + s4, sc = j * 32 + lr - s4;
-                        *reinterpret_cast<uint2*>(wl + sr * kStride + sc * 2) = make_uint2(lo, hi);
+                        *reinterpret_cast<uint2*>(wl + sr * kStrideN + sc * 2) = make_uint2(lo, hi);
                     }
-            drain(out_n, ld_n, ti * TILE + wm * kW, tj * TILE + wn * kW);
+            drain(out_n, ld_n, ti * TILE + wm * kWm, tj * TILE + wn * kWn, kWn, kStrideN, kWm);
         } else {
 #pragma unroll
-            for (int i = 0; i < kNf; ++i) {
+            for (int i = 0; i < kMi; ++i) {
 #pragma unroll
-                for (int j = 0; j < kNf; ++j) {
+                for (int j = 0; j < kNj; ++j) {
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const int gi = row0 + i * 32 + g * 8;
@@ -418,9 +434,9 @@ __global__ __launch_bounds__(256) void ns_gemm_kernel(NsArgs args) {
         const int r = mt.r, c = mt.c;
         const bool tall = mt.tall != 0;
 #pragma unroll
-        for (int i = 0; i < kNf; ++i) {
+        for (int i = 0; i < kMi; ++i) {
 #pragma unroll
-            for (int j = 0; j < kNf; ++j) {
+            for (int j = 0; j < kNj; ++j) {
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int gi = row0 + i * 32 + g * 8;
@@ -482,7 +498,7 @@ template <int TILE, bool BF16>
 hipError_t launch_stage(int stage, int n_tiles, const NsArgs& a, hipStream_t s) {
     if (n_tiles == 0) return hipSuccess;
     LaunchTimer timer(stage_name<TILE, BF16>(stage), s);
-    const dim3 grid{static_cast<unsigned>(n_tiles)}, block{256};
+    const dim3 grid{static_cast<unsigned>(n_tiles)}, block{unsigned(Geo<TILE, BF16>::kThreads)};
     switch (stage) {
         case kStageA: ns_gemm_kernel<TILE, BF16, kStageA><<<grid, block, 0, s>>>(a); break;
         case kStageB: ns_gemm_kernel<TILE, BF16, kStageB><<<grid, block, 0, s>>>(a); break;
