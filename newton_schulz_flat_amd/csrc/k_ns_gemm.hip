@@ -96,6 +96,25 @@ __device__ __forceinline__ void store4(uint16_t* p, const float v[4]) {
     *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
 }
 
+// Raw (undecoded) 4-element operand vectors: loaded in batches so that one
+// wave pays one memory latency per batch, not one per vector.
+template <typename TE> struct Raw4;
+template <> struct Raw4<uint16_t> { uint2 v; };
+template <> struct Raw4<float> { float4 v; };
+__device__ __forceinline__ Raw4<uint16_t> load_raw4(const uint16_t* p) {
+    return {*reinterpret_cast<const uint2*>(p)};
+}
+__device__ __forceinline__ Raw4<float> load_raw4(const float* p) {
+    return {*reinterpret_cast<const float4*>(p)};
+}
+__device__ __forceinline__ void decode4(const Raw4<uint16_t>& r, float v[4]) {
+    v[0] = __uint_as_float(r.v.x << 16), v[1] = __uint_as_float(r.v.x & 0xffff0000u);
+    v[2] = __uint_as_float(r.v.y << 16), v[3] = __uint_as_float(r.v.y & 0xffff0000u);
+}
+__device__ __forceinline__ void decode4(const Raw4<float>& r, float v[4]) {
+    v[0] = r.v.x, v[1] = r.v.y, v[2] = r.v.z, v[3] = r.v.w;
+}
+
 // Quad transpose: lanes 4m+s (s = 0..3, same half-wave) each hold one column
 // of a 4 x 4 block, v[t] = M[t][s]; afterwards lane 4m+s holds row s,
 // w[t] = M[s][t].  Two DPP butterflies (xor 2, then xor 1) and a final
@@ -328,26 +347,41 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
             static_assert(kRegion * G::kWaves <= 2 * 2 * G::kOp, "epilogue staging exceeds LDS");
             unsigned char* wl = lds + wave * kRegion;
             uint32_t pk[kMi][kNj][4][2];
+            constexpr int kIB = kMi > 1 ? kMi / 2 : 1;  // fragment rows per load batch
 #pragma unroll
-            for (int i = 0; i < kMi; ++i) {
+            for (int i0 = 0; i0 < kMi; i0 += kIB) {
+                Raw4<TE> raw[kIB][kNj][4];
+                if (STAGE != kStageA) {
 #pragma unroll
-                for (int j = 0; j < kNj; ++j) {
+                    for (int ii = 0; ii < kIB; ++ii)
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int gi = row0 + i * 32 + g * 8;
-                        const int gj = col0 + j * 32;
-                        float v[4];
+                        for (int j = 0; j < kNj; ++j)
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) v[t] = acc[i][j][g * 4 + t];
-                        if (STAGE != kStageA) {
-                            float ov[4];
-                            load4(opnd + int64_t(gj) * rp + gi, ov);
+                            for (int g = 0; g < 4; ++g)
+                                raw[ii][j][g] = load_raw4(opnd + int64_t(col0 + j * 32) * rp +
+                                                          row0 + (i0 + ii) * 32 + g * 8);
+                }
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                            for (int t = 0; t < 4; ++t)
-                                v[t] = STAGE == kStageB ? cb * ov[t] + cc * v[t] : ca * ov[t] + v[t];
+                for (int ii = 0; ii < kIB; ++ii) {
+                    const int i = i0 + ii;
+#pragma unroll
+                    for (int j = 0; j < kNj; ++j) {
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            float v[4];
+#pragma unroll
+                            for (int t = 0; t < 4; ++t) v[t] = acc[i][j][g * 4 + t];
+                            if (STAGE != kStageA) {
+                                float ov[4];
+                                decode4(raw[ii][j][g], ov);
+#pragma unroll
+                                for (int t = 0; t < 4; ++t)
+                                    v[t] = STAGE == kStageB ? cb * ov[t] + cc * v[t] : ca * ov[t] + v[t];
+                            }
+                            pk[i][j][g][0] = uint32_t(bf16_rne(v[0])) | (uint32_t(bf16_rne(v[1])) << 16);
+                            pk[i][j][g][1] = uint32_t(bf16_rne(v[2])) | (uint32_t(bf16_rne(v[3])) << 16);
                         }
-                        pk[i][j][g][0] = uint32_t(bf16_rne(v[0])) | (uint32_t(bf16_rne(v[1])) << 16);
-                        pk[i][j][g][1] = uint32_t(bf16_rne(v[2])) | (uint32_t(bf16_rne(v[3])) << 16);
                     }
                 }
             }
@@ -402,6 +436,15 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
         } else {
 #pragma unroll
             for (int i = 0; i < kMi; ++i) {
+                Raw4<TE> raw[kNj][4];
+                if (STAGE != kStageA) {
+#pragma unroll
+                    for (int j = 0; j < kNj; ++j)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g)
+                            raw[j][g] = load_raw4(opnd + int64_t(col0 + j * 32) * rp + row0 + i * 32 + g * 8);
+                }
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int j = 0; j < kNj; ++j) {
 #pragma unroll
@@ -413,7 +456,7 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                         for (int t = 0; t < 4; ++t) v[t] = acc[i][j][g * 4 + t];
                         if (STAGE != kStageA) {
                             float ov[4];
-                            load4(opnd + int64_t(gj) * rp + gi, ov);
+                            decode4(raw[j][g], ov);
 #pragma unroll
                             for (int t = 0; t < 4; ++t)
                                 v[t] = STAGE == kStageB ? cb * ov[t] + cc * v[t] : ca * ov[t] + v[t];
@@ -435,6 +478,13 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
         const bool tall = mt.tall != 0;
 #pragma unroll
         for (int i = 0; i < kMi; ++i) {
+            Raw4<TE> raw[kNj][4];
+#pragma unroll
+            for (int j = 0; j < kNj; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    raw[j][g] = load_raw4(xt + int64_t(col0 + j * 32) * rp + row0 + i * 32 + g * 8);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < kNj; ++j) {
 #pragma unroll
@@ -442,7 +492,7 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                     const int gi = row0 + i * 32 + g * 8;
                     const int gj = col0 + j * 32;
                     float v[4], xv[4];
-                    load4(xt + int64_t(gj) * rp + gi, xv);
+                    decode4(raw[j][g], xv);
 #pragma unroll
                     for (int t = 0; t < 4; ++t) v[t] = sc * (ca * xv[t] + acc[i][j][g * 4 + t]);
                     if (tall) {
