@@ -54,7 +54,7 @@ def elementwise_bytes(wl):
     n = wl.numel()
     wb = 2 if wl.param_dtype == "bf16" else 4
     return {"front": 16 * n,           # G read, M read + write, U write (float32)
-            "cast": 4 * n + 2 * 2 * n,  # U read, X0 and X0^T written (bf16)
+            "cast": 4 * n + 2 * n,      # U read, X0 written (bf16)
             "apply": 4 * n + 2 * wb * n}  # O read, W read + write
 
 

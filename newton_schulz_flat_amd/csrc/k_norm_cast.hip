@@ -5,13 +5,12 @@
 // sums of squares in a fixed order and stores inv = 1 / (sqrt(sum) + 1e-7).
 //
 // cast_kernel: one workgroup per 64 x 64 tile of the padded NS-orientation
-// matrix (rp x cp).  It reads the matching 64 x 64 block of U in U's own
+// matrix X0 (rp x cp).  It reads the matching 64 x 64 block of U in U's own
 // row-major orientation (coalesced along U's rows), scales it by inv, and
-// writes both X0 (rp x cp) and X0^T (cp x rp) -- the two layouts the GEMM
-// stages read -- through an LDS transpose, so every global access runs along
-// a row.  Tall matrices (rows > cols) are transposed into the wide
-// orientation here.  Elements outside the r x c matrix are written as zero,
-// which the Newton-Schulz products preserve.  With ns_steps == 0 it writes
+// writes X0 along its rows, transposing through LDS when the matrix is tall
+// (rows > cols: tall matrices are transposed into the wide orientation here).
+// Elements outside the r x c matrix are written as zero, which the
+// Newton-Schulz products preserve.  With ns_steps == 0 it writes
 // O = fl(s * X0) in U's own layout instead.
 #include "k_common.h"
 
@@ -42,6 +41,14 @@ __global__ __launch_bounds__(kNormThreads) void norm_kernel(const MatInfo* __res
 
 __device__ __forceinline__ void store_x(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_x(uint16_t* p, float v) { *p = bf16_rne(v); }
+__device__ __forceinline__ void store_x4(float* p, const float v[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void store_x4(uint16_t* p, const float v[4]) {
+    const uint32_t lo = uint32_t(bf16_rne(v[0])) | (uint32_t(bf16_rne(v[1])) << 16);
+    const uint32_t hi = uint32_t(bf16_rne(v[2])) | (uint32_t(bf16_rne(v[3])) << 16);
+    *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+}
 __device__ __forceinline__ float rounded(float v, float*) { return v; }
 __device__ __forceinline__ float rounded(float v, uint16_t*) { return bf16_to_f32(bf16_rne(v)); }
 
@@ -50,8 +57,7 @@ __global__ __launch_bounds__(256) void cast_kernel(const MatInfo* __restrict__ m
                                                    const int32_t* __restrict__ prefix, int n,
                                                    const float* u,  // may equal o_direct
                                                    const float* __restrict__ inv,
-                                                   TX* __restrict__ x, TX* __restrict__ xt,
-                                                   float* o_direct) {
+                                                   TX* __restrict__ x, float* o_direct) {
     constexpr int T = kCastTile;
     __shared__ float tile[T][T + 1];
     const int blk = blockIdx.x;
@@ -86,18 +92,14 @@ __global__ __launch_bounds__(256) void cast_kernel(const MatInfo* __restrict__ m
         return;
     }
     TX* xm = x + mt.x_off;
-    TX* xtm = xt + mt.x_off;
-    // X0[i][j], i = ti*T + a, j = tj*T + b  (native element tile[a][b] or tile[b][a])
-    for (int idx = threadIdx.x; idx < T * T; idx += 256) {
-        const int a = idx / T, b = idx % T;
-        const float v = tall ? tile[b][a] : tile[a][b];
-        store_x(xm + int64_t(ti * T + a) * mt.cp + tj * T + b, v);
-    }
-    // X0^T[j][i], j = tj*T + a, i = ti*T + b
-    for (int idx = threadIdx.x; idx < T * T; idx += 256) {
-        const int a = idx / T, b = idx % T;
-        const float v = tall ? tile[a][b] : tile[b][a];
-        store_x(xtm + int64_t(tj * T + a) * mt.rp + ti * T + b, v);
+    // X0[i][j], i = ti*T + a, j = tj*T + b  (native element tile[a][b] or tile[b][a]);
+    // each thread writes 4 consecutive elements of a row
+    for (int idx = threadIdx.x; idx < T * T / 4; idx += 256) {
+        const int a = idx / (T / 4), b = (idx % (T / 4)) * 4;
+        float v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = tall ? tile[b + t][a] : tile[a][b + t];
+        store_x4(xm + int64_t(ti * T + a) * mt.cp + tj * T + b, v);
     }
 }
 
@@ -118,13 +120,11 @@ hipError_t launch_cast(const PlanView& p, const float* u, const float* inv, void
     const dim3 grid{static_cast<unsigned>(p.total_cast)}, block{256};
     if (p.gemm_mode == MUON_GEMM_F32)
         cast_kernel<float><<<grid, block, 0, s>>>(p.mats, p.cast_prefix, p.n, u, inv,
-                                                  reinterpret_cast<float*>(w + p.ws.x),
-                                                  reinterpret_cast<float*>(w + p.ws.xt[0]),
+                                                  reinterpret_cast<float*>(w + p.ws.x[0]),
                                                   o_direct);
     else
         cast_kernel<uint16_t><<<grid, block, 0, s>>>(p.mats, p.cast_prefix, p.n, u, inv,
-                                                     reinterpret_cast<uint16_t*>(w + p.ws.x),
-                                                     reinterpret_cast<uint16_t*>(w + p.ws.xt[0]),
+                                                     reinterpret_cast<uint16_t*>(w + p.ws.x[0]),
                                                      o_direct);
     return hipGetLastError();
 }

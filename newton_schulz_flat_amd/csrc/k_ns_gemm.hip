@@ -8,18 +8,23 @@
 //   stage B   B = b A + c A A^T    P = Q = A   (rp x rp), K = rp   symmetric
 //   stage X   X <- a X + B X       P = B, Q = X^T (cp x rp), K = rp
 //
-// (A is symmetric, so A A = A A^T, and B X = B (X^T)^T.)  Keeping X^T next to
-// X makes every operand load a contiguous run along K, which is exactly what
-// the MFMA operand layout wants (8 consecutive K values per lane for bf16).
+// (A is symmetric, so A A = A A^T, and B X = B (X^T)^T.)  The MFMA operand
+// layout wants each lane to hold consecutive K values of one operand row (8
+// for bf16), so operand tiles are staged in LDS as rows along K.  For P and
+// for the symmetric stages those are rows of the stored matrices; stage X's
+// Q = X^T is never stored: its loader reads blocks of consecutive rows of X
+// (a few K values by 16 bytes of columns) and transposes them in registers on
+// their way into LDS.
 //
 // Symmetric stages compute only tiles with ti <= tj and mirror each
 // off-diagonal tile into (tj, ti).  The axpys b A + c (.) and a X + (.) run in
-// float32 in the epilogues; the stage-B epilogue reads A and the stage-X
-// epilogue reads X from the transposed copies, whose 4 consecutive elements
-// match the 4 consecutive output rows each lane holds.  Stage X writes X in
-// place (no workgroup reads X during stage X) and X^T into the other
-// ping-pong buffer; on the last iteration it writes O = fl(s * X) in the
-// matrix's original orientation instead.
+// float32 in the epilogues; the stage-B epilogue reads A along a column
+// (A is symmetric), whose 4 consecutive elements match the 4 consecutive
+// output rows each lane holds; the stage-X epilogue first exchanges its
+// results across lane quads into row order and then reads X along rows.
+// X ping-pongs between two buffers (workgroups of stage X still read the
+// current X while others write the next one); on the last iteration stage X
+// writes O = fl(s * X) in the matrix's original orientation instead.
 //
 // Workgroup: 4 waves in a 2 x 2 grid over a TILE x TILE output tile (8 waves,
 // 2 x 4, for the 256 x 256 bf16 tile); each wave owns its block of outputs as
@@ -44,9 +49,8 @@ enum Stage { kStageA = 0, kStageB = 1, kStageX = 2 };
 struct NsArgs {
     const MatInfo* mats;
     const GemmTile* tiles;
-    void* x;        // X region
-    void* xt_cur;   // X^T read by this iteration
-    void* xt_next;  // X^T written by this iteration
+    const void* x_cur;  // X read by this iteration
+    void* x_next;       // X written by this iteration (unused on the last)
     void* ga;       // A region
     void* gb;       // B region
     float* o;       // O (last iteration), laid out like the gradients
@@ -146,6 +150,42 @@ __device__ __forceinline__ void quad_transpose(const float v[4], float w[4], int
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Two transposing LDS reads (ds_read_b64_tr_b16) at p and p + second, as one
+// 8-element MFMA operand.  p points into LDS.
+__device__ __forceinline__ u32x4 read_tr(const unsigned char* p, int second) {
+    const uint2 lo = __builtin_bit_cast(
+        uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(const_cast<unsigned char*>(p))));
+    const uint2 hi = __builtin_bit_cast(
+        uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(const_cast<unsigned char*>(p + second))));
+    return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
+
+// LDS write number w of a thread's Q operand chunks of one K block, at dst.
+// Row copies: chunk w (16 bytes of one row) goes to row pass w, `pass` bytes
+// apart.  Transposed (float32 stage X): pb[l] holds 4 columns of K row l of
+// the thread's block; operand row c (one column of X) takes element c of
+// every pb[l], l = 0..kL-1, as kL consecutive K values.
+template <bool TRANS, int kL>
+__device__ __forceinline__ void store_q(unsigned char* dst, const u32x4 (&pb)[kL], int w, int pass) {
+    if constexpr (!TRANS) {
+        *reinterpret_cast<u32x4*>(dst + w * pass) = pb[w];
+    } else {
+        {
+            if constexpr (kL == 8) {
+                const int c = w >> 1, h = (w & 1) * 4;
+                *reinterpret_cast<u32x4*>(dst + c * kLdsStride + h * 4) =
+                    u32x4{pb[h][c], pb[h + 1][c], pb[h + 2][c], pb[h + 3][c]};
+            } else if constexpr (kL == 4) {
+                *reinterpret_cast<u32x4*>(dst + w * kLdsStride) = u32x4{pb[0][w], pb[1][w], pb[2][w], pb[3][w]};
+            } else {
+                *reinterpret_cast<uint2*>(dst + w * kLdsStride) = make_uint2(pb[0][w], pb[1][w]);
+            }
+        }
+    }
+}
 
 template <int TILE, bool BF16, int STAGE>
 __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(NsArgs args) {
@@ -155,7 +195,19 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
     constexpr int kBk = kRowBytes / kEs;  // K elements per block
     constexpr int kMi = G::kMi, kNj = G::kNj;
     constexpr int kL = G::kLoads;
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * 2 * G::kOp];
+    // How stage X stages its Q = X^T; every other operand is a copy of rows.
+    //  bf16: K rows of X are copied as they are (an LDS row of kS bytes holds the
+    //        tile's TILE columns of one K row) and the fragment reads transpose
+    //        them with ds_read_b64_tr_b16;
+    //  f32:  blocks of X are transposed in registers on their way into LDS.
+    constexpr bool kQLdsT = STAGE == kStageX && BF16;
+    constexpr bool kTransQ = STAGE == kStageX && !BF16;
+    // kS = 64 (mod 256) bytes: the four K rows one transposing read gathers
+    // start in distinct quarters of the 256-byte bank space
+    constexpr int kS = TILE * 2 + 64;
+    constexpr int kOpQ = (kQLdsT && kBk * kS > G::kOp) ? kBk * kS : G::kOp;
+    constexpr int kBuf = G::kOp + kOpQ;  // one stage of the double-buffered operands
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kBuf];
 
     const GemmTile tile = args.tiles[blockIdx.x];
     if (tile.mat < 0) return;  // padding slot of the XCD-interleaved table
@@ -163,11 +215,12 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
     const int rp = mt.rp, cp = mt.cp;
     const int ti = tile.ti, tj = tile.tj;
 
+    // Stage X reads its Q operand transposed out of row-major X (see above).
     const TE* P;
     const TE* Q;
     int ld, K;
     if (STAGE == kStageA) {
-        const TE* base = static_cast<const TE*>(args.x) + mt.x_off;
+        const TE* base = static_cast<const TE*>(args.x_cur) + mt.x_off;
         P = base + int64_t(ti) * TILE * cp;
         Q = base + int64_t(tj) * TILE * cp;
         ld = cp;
@@ -180,7 +233,7 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
         K = rp;
     } else {
         P = static_cast<const TE*>(args.gb) + mt.g_off + int64_t(ti) * TILE * rp;
-        Q = static_cast<const TE*>(args.xt_cur) + mt.x_off + int64_t(tj) * TILE * rp;
+        Q = static_cast<const TE*>(args.x_cur) + mt.x_off + int64_t(tj) * TILE;  // X[k][tj*TILE + .]
         ld = rp;
         K = rp;
     }
@@ -189,17 +242,50 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
     const int wm = wave & 1, wn = wave >> 1;
     const int lr = lane & 31, hk = lane >> 5;
 
-    // Global -> LDS staging: thread tid moves 16-byte chunk (tid & 7) of rows
-    // (tid >> 3) + l * kRowsPerPass, l = 0..kL-1, of each operand's K block.
+    // Global -> LDS staging of row operands: thread tid moves 16-byte chunk
+    // (tid & 7) of rows (tid >> 3) + l * kRowsPerPass, l = 0..kL-1, of the
+    // operand's K block.
     const int lrow = tid >> 3, lchunk = tid & 7;
     const TE* gp = P + int64_t(lrow) * ld + lchunk * (16 / kEs);
-    const TE* gq = Q + int64_t(lrow) * ld + lchunk * (16 / kEs);
     const int64_t rstep = int64_t(G::kRowsPerPass) * ld;
     const int lds_st = lrow * kLdsStride + lchunk * 16;
     constexpr int kLdsPass = G::kRowsPerPass * kLdsStride;
+    // Register-transposed staging (float32 stage X): thread tid loads K rows
+    // kg*kL .. kg*kL+kL-1 of X at the 16-byte column chunk jb, i.e. a kL x kCpc
+    // block, and writes it as kCpc operand rows (jb*kCpc + c) of kL elements
+    // each at K offset kg*kL.  Consecutive threads take consecutive kg, so the
+    // LDS writes of one wave cover whole 128-byte rows.
+    constexpr int kCpc = 16 / kEs;    // elements per 16-byte chunk
+    constexpr int kNkg = kBk / kL;    // K-row groups per K block
+    static_assert(!kTransQ || kNkg * (TILE / kCpc) == G::kThreads, "transposed loader covers the tile");
+    static_assert(!kTransQ || kL == 2 || kL == 4 || kL == 8, "transposed loader block height");
+    const int kg = tid % kNkg, jb = tid / kNkg;
+    // LDS writes of Q per thread and K block: one per row operand chunk, or one per
+    // transposed row (two for float32 rows of 8 elements)
+    constexpr int kQW = !kTransQ ? kL : kL < 8 ? kCpc : 2 * kCpc;
+    // X-row staging (bf16 stage X): thread tid moves 16-byte chunk (tid % kQc) of
+    // K rows tid / kQc + l * kQr of the K block.
+    constexpr int kQc = TILE * kEs / 16, kQr = G::kThreads / kQc;
+    static_assert(!kQLdsT || kQr * kL == kBk, "X-row loader covers the K block");
+    const int qrow = tid / kQc, qch = tid % kQc;
+    const TE* gq = kTransQ ? Q + int64_t(kg * kL) * cp + jb * kCpc
+                   : kQLdsT ? Q + int64_t(qrow) * cp + qch * kCpc
+                            : Q + int64_t(lrow) * ld + lchunk * (16 / kEs);
+    // between a thread's Q loads
+    const int64_t qstep = kTransQ ? int64_t(cp) : kQLdsT ? int64_t(kQr) * cp : rstep;
+    const int q_st = G::kOp + (kTransQ   ? jb * kCpc * kLdsStride + kg * kL * kEs
+                               : kQLdsT ? qrow * kS + qch * 16
+                                        : lds_st);
+    const int q_pass = kQLdsT ? kQr * kS : kLdsPass;
     // Fragment reads: row lr of each 32-row fragment, bytes [hk*64, hk*64 + 64).
     const int fa_off = (wm * G::kWm + lr) * kLdsStride + hk * 64;
     const int fb_off = G::kOp + (wn * G::kWn + lr) * kLdsStride + hk * 64;
+    // Transposing reads (bf16 stage X): within each 16-lane group, lane g reads
+    // 4 elements of K row (g >> 2) at column 4 (g & 3) and receives column g of
+    // the 4 x 16 block; a lane thus gets 4 consecutive K values of operand row
+    // lr, and two reads (K rows +0 and +4) make the 8 the MFMA takes.
+    const int fbt_off = G::kOp + (hk * 32 + ((lane & 15) >> 2)) * kS +
+                        (wn * G::kWn + (lane & 16) + (lane & 3) * 4) * 2;
 
     f32x16 acc[kMi][kNj];
 #pragma unroll
@@ -213,13 +299,12 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
 #pragma unroll
     for (int l = 0; l < kL; ++l) {
         pa[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep);
-        pb[l] = *reinterpret_cast<const u32x4*>(gq + l * rstep);
+        pb[l] = *reinterpret_cast<const u32x4*>(gq + l * qstep);
     }
 #pragma unroll
-    for (int l = 0; l < kL; ++l) {
-        *reinterpret_cast<u32x4*>(lds + lds_st + l * kLdsPass) = pa[l];
-        *reinterpret_cast<u32x4*>(lds + G::kOp + lds_st + l * kLdsPass) = pb[l];
-    }
+    for (int l = 0; l < kL; ++l) *reinterpret_cast<u32x4*>(lds + lds_st + l * kLdsPass) = pa[l];
+#pragma unroll
+    for (int w = 0; w < kQW; ++w) store_q<kTransQ, kL>(lds + q_st, pb, w, q_pass);
     __syncthreads();
 
     // Main loop.  One K block is a single basic block whose instruction order
@@ -238,11 +323,13 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
         fa[0][i] = *reinterpret_cast<const u32x4*>(lds + fa_off + i * 32 * kLdsStride);
 #pragma unroll
     for (int j = 0; j < kNj; ++j)
-        fb[0][j] = *reinterpret_cast<const u32x4*>(lds + fb_off + j * 32 * kLdsStride);
+        fb[0][j] = kQLdsT ? read_tr(lds + fbt_off + j * 64, 4 * kS)
+                          : *reinterpret_cast<const u32x4*>(lds + fb_off + j * 32 * kLdsStride);
     for (int kb = 0; kb < nkb; ++kb) {
         const int64_t k0 = int64_t(kb + 1 < nkb ? kb + 1 : kb) * kBk;
-        const unsigned char* buf = lds + (kb & 1) * 2 * G::kOp;
-        unsigned char* nbuf = lds + ((kb + 1) & 1) * 2 * G::kOp;
+        const int64_t qk = (kTransQ || kQLdsT) ? k0 * cp : k0;  // Q offset of the next block
+        const unsigned char* buf = lds + (kb & 1) * kBuf;
+        unsigned char* nbuf = lds + ((kb + 1) & 1) * kBuf;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int cur = q & 1;
@@ -267,6 +354,9 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                         if (rd < kMi)
                             fa[cur ^ 1][rd] = *reinterpret_cast<const u32x4*>(
                                 buf + fa_off + rd * 32 * kLdsStride + at);
+                        else if (kQLdsT)
+                            fb[cur ^ 1][rd - kMi] =
+                                read_tr(buf + fbt_off + (rd - kMi) * 64 + (q + 1) * 8 * kS, 4 * kS);
                         else
                             fb[cur ^ 1][rd - kMi] = *reinterpret_cast<const u32x4*>(
                                 buf + fb_off + (rd - kMi) * 32 * kLdsStride + at);
@@ -278,17 +368,16 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                         if (l < kL)
                             pa[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep + k0);
                         else
-                            pb[l - kL] = *reinterpret_cast<const u32x4*>(gq + (l - kL) * rstep + k0);
+                            pb[l - kL] = *reinterpret_cast<const u32x4*>(gq + (l - kL) * qstep + qk);
                     }
                 }
                 if (q == 3) {
 #pragma unroll
-                    for (int l = m; l < 2 * kL; l += kMfma) {
+                    for (int l = m; l < kL + kQW; l += kMfma) {
                         if (l < kL)
                             *reinterpret_cast<u32x4*>(nbuf + lds_st + l * kLdsPass) = pa[l];
                         else
-                            *reinterpret_cast<u32x4*>(nbuf + G::kOp + lds_st + (l - kL) * kLdsPass) =
-                                pb[l - kL];
+                            store_q<kTransQ, kL>(nbuf + q_st, pb, l - kL, q_pass);
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -301,50 +390,54 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
             fa[0][i] = *reinterpret_cast<const u32x4*>(nbuf + fa_off + i * 32 * kLdsStride);
 #pragma unroll
         for (int j = 0; j < kNj; ++j)
-            fb[0][j] = *reinterpret_cast<const u32x4*>(nbuf + fb_off + j * 32 * kLdsStride);
+            fb[0][j] = kQLdsT ? read_tr(nbuf + fbt_off + j * 64, 4 * kS)
+                              : *reinterpret_cast<const u32x4*>(nbuf + fb_off + j * 32 * kLdsStride);
     }
 
     // Epilogue.  Lane (lr, hk) of fragment (i, j) holds, for g = 0..3, the
-    // outputs at rows gi + 0..3 (gi = wave row + i*32 + g*8 + hk*4) of column gj.
-    // Column-oriented stores take those 4 values as one vector; row-oriented
-    // stores first exchange them across the lane quad so that lane s of the
-    // quad holds row gi + s, columns gj - s .. gj - s + 3.
+    // outputs at rows gi + 0..3 (gi = wave row + i*32 + g*8 + hk*4) of column gj
+    // (column layout).  Column-oriented stores take those 4 values as one
+    // vector; the row layout comes from exchanging them across the lane quad,
+    // after which lane s of the quad holds row gi + s, columns gj - s .. gj - s + 3.
+    // Stage X works in the row layout throughout, so that its operand X is read
+    // along rows.
     const int s4 = lr & 3;
     const int row0 = ti * TILE + wm * G::kWm + hk * 4;
     const int col0 = tj * TILE + wn * G::kWn + lr;
     const float ca = args.ca, cb = args.cb, cc = args.cc;
+    const TE* xc = static_cast<const TE*>(args.x_cur) + mt.x_off;
+    // X (row layout) at fragment (i, j), group g
+    auto x_row = [&](int i, int j, int g) {
+        return xc + int64_t(row0 + i * 32 + g * 8 + s4) * cp + (col0 + j * 32 - s4);
+    };
     if (STAGE != kStageX || !args.last) {
         TE* out_n;  // row-oriented destination, leading dimension ld_n
-        TE* out_t;  // column-oriented destination, leading dimension ld_t
-        int ld_n, ld_t;
+        int ld_n;
         if (STAGE == kStageX) {
-            out_n = static_cast<TE*>(args.x) + mt.x_off;
-            out_t = static_cast<TE*>(args.xt_next) + mt.x_off;
+            out_n = static_cast<TE*>(args.x_next) + mt.x_off;
             ld_n = cp;
-            ld_t = rp;
         } else {
             out_n = static_cast<TE*>(STAGE == kStageA ? args.ga : args.gb) + mt.g_off;
-            out_t = out_n;
             ld_n = rp;
-            ld_t = rp;
         }
-        const bool write_t = STAGE == kStageX || ti != tj;
-        const TE* opnd = nullptr;  // epilogue operand, read column-oriented
-        if (STAGE == kStageB) opnd = static_cast<const TE*>(args.ga) + mt.g_off;
-        if (STAGE == kStageX) opnd = static_cast<const TE*>(args.xt_cur) + mt.x_off;
+        TE* const out_t = out_n;  // mirror (symmetric stages), leading dimension rp
+        const bool write_t = STAGE != kStageX && ti != tj;
+        // stage-B operand A, read along a column (A is symmetric)
+        const TE* ga = static_cast<const TE*>(args.ga) + mt.g_off;
         if constexpr (BF16) {
             // bfloat16 outputs go through LDS so that every global store writes
             // 16 contiguous bytes per lane along an output row.  Each wave stages its
             // own kWm x kWn sub-tile (rows padded by 16 bytes) in a private region:
-            // first in the column-oriented layout (for out_t), then in the
-            // row-oriented layout (for out_n, via the quad exchange).  The values
-            // are rounded to bfloat16 once and kept packed in registers between
-            // the two passes.  The main loop ended with a barrier, so LDS is free.
+            // for a mirrored tile first in the column layout (for out_t), then in
+            // the row layout (for out_n).  The values are rounded to bfloat16 once
+            // and kept packed in registers between the two passes (in the row
+            // layout already for stage X).  The main loop ended with a barrier, so
+            // LDS is free.
             constexpr int kWm = G::kWm, kWn = G::kWn;
             constexpr int kStrideT = kWm * 2 + 16;  // column-oriented: kWn rows of kWm
             constexpr int kStrideN = kWn * 2 + 16;  // row-oriented: kWm rows of kWn
             constexpr int kRegion = (kWn * kStrideT > kWm * kStrideN) ? kWn * kStrideT : kWm * kStrideN;
-            static_assert(kRegion * G::kWaves <= 2 * 2 * G::kOp, "epilogue staging exceeds LDS");
+            static_assert(kRegion * G::kWaves <= 2 * kBuf, "epilogue staging exceeds LDS");
             unsigned char* wl = lds + wave * kRegion;
             uint32_t pk[kMi][kNj][4][2];
             constexpr int kIB = kMi > 1 ? kMi / 2 : 1;  // fragment rows per load batch
@@ -358,8 +451,10 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                         for (int j = 0; j < kNj; ++j)
 #pragma unroll
                             for (int g = 0; g < 4; ++g)
-                                raw[ii][j][g] = load_raw4(opnd + int64_t(col0 + j * 32) * rp +
-                                                          row0 + (i0 + ii) * 32 + g * 8);
+                                raw[ii][j][g] = STAGE == kStageX
+                                                    ? load_raw4(x_row(i0 + ii, j, g))
+                                                    : load_raw4(ga + int64_t(col0 + j * 32) * rp + row0 +
+                                                                (i0 + ii) * 32 + g * 8);
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -372,12 +467,17 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                             float v[4];
 #pragma unroll
                             for (int t = 0; t < 4; ++t) v[t] = acc[i][j][g * 4 + t];
-                            if (STAGE != kStageA) {
+                            if (STAGE == kStageX) {
+                                float w[4], ov[4];
+                                quad_transpose(v, w, s4);
+                                decode4(raw[ii][j][g], ov);
+#pragma unroll
+                                for (int t = 0; t < 4; ++t) v[t] = ca * ov[t] + w[t];
+                            } else if (STAGE == kStageB) {
                                 float ov[4];
                                 decode4(raw[ii][j][g], ov);
 #pragma unroll
-                                for (int t = 0; t < 4; ++t)
-                                    v[t] = STAGE == kStageB ? cb * ov[t] + cc * v[t] : ca * ov[t] + v[t];
+                                for (int t = 0; t < 4; ++t) v[t] = cb * ov[t] + cc * v[t];
                             }
                             pk[i][j][g][0] = uint32_t(bf16_rne(v[0])) | (uint32_t(bf16_rne(v[1])) << 16);
                             pk[i][j][g][1] = uint32_t(bf16_rne(v[2])) | (uint32_t(bf16_rne(v[3])) << 16);
@@ -401,7 +501,7 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             };
             if (write_t) {
-                // column-oriented: staged row = output column j*32 + lr, 4 rows per lane
+                // column layout: staged row = output column j*32 + lr, 4 rows per lane
 #pragma unroll
                 for (int i = 0; i < kMi; ++i)
 #pragma unroll
@@ -412,23 +512,26 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                             *reinterpret_cast<uint2*>(wl + sr * kStrideT + sc * 2) =
                                 make_uint2(pk[i][j][g][0], pk[i][j][g][1]);
                         }
-                drain(out_t, ld_t, tj * TILE + wn * kWn, ti * TILE + wm * kWm, kWm, kStrideT, kWn);
+                drain(out_t, rp, tj * TILE + wn * kWn, ti * TILE + wm * kWm, kWm, kStrideT, kWn);
             }
-            // row-oriented: after the quad exchange lane s holds row (.. + s), columns c - s ..
+            // row layout: lane s holds row (.. + s), columns c - s ..
 #pragma unroll
             for (int i = 0; i < kMi; ++i)
 #pragma unroll
                 for (int j = 0; j < kNj; ++j)
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
-                        float v[4], w[4];
-                        v[0] = __uint_as_float(pk[i][j][g][0] << 16);
-                        v[1] = __uint_as_float(pk[i][j][g][0] & 0xffff0000u);
-                        v[2] = __uint_as_float(pk[i][j][g][1] << 16);
-                        v[3] = __uint_as_float(pk[i][j][g][1] & 0xffff0000u);
-                        quad_transpose(v, w, s4);
-                        const uint32_t lo = (__float_as_uint(w[0]) >> 16) | (__float_as_uint(w[1]) & 0xffff0000u);
-                        const uint32_t hi = (__float_as_uint(w[2]) >> 16) | (__float_as_uint(w[3]) & 0xffff0000u);
+                        uint32_t lo = pk[i][j][g][0], hi = pk[i][j][g][1];
+                        if (STAGE != kStageX) {
+                            float v[4], w[4];
+                            v[0] = __uint_as_float(lo << 16);
+                            v[1] = __uint_as_float(lo & 0xffff0000u);
+                            v[2] = __uint_as_float(hi << 16);
+                            v[3] = __uint_as_float(hi & 0xffff0000u);
+                            quad_transpose(v, w, s4);
+                            lo = (__float_as_uint(w[0]) >> 16) | (__float_as_uint(w[1]) & 0xffff0000u);
+                            hi = (__float_as_uint(w[2]) >> 16) | (__float_as_uint(w[3]) & 0xffff0000u);
+                        }
                         const int sr = i * 32 + g * 8 + hk * 4 + s4, sc = j * 32 + lr - s4;
                         *reinterpret_cast<uint2*>(wl + sr * kStrideN + sc * 2) = make_uint2(lo, hi);
                     }
@@ -442,7 +545,9 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                     for (int j = 0; j < kNj; ++j)
 #pragma unroll
                         for (int g = 0; g < 4; ++g)
-                            raw[j][g] = load_raw4(opnd + int64_t(col0 + j * 32) * rp + row0 + i * 32 + g * 8);
+                            raw[j][g] = STAGE == kStageX
+                                            ? load_raw4(x_row(i, j, g))
+                                            : load_raw4(ga + int64_t(col0 + j * 32) * rp + row0 + i * 32 + g * 8);
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -451,27 +556,30 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                     for (int g = 0; g < 4; ++g) {
                         const int gi = row0 + i * 32 + g * 8;
                         const int gj = col0 + j * 32;
-                        float v[4];
+                        float v[4], w[4], ov[4];
 #pragma unroll
                         for (int t = 0; t < 4; ++t) v[t] = acc[i][j][g * 4 + t];
-                        if (STAGE != kStageA) {
-                            float ov[4];
+                        if (STAGE == kStageX) {
+                            quad_transpose(v, w, s4);
                             decode4(raw[j][g], ov);
 #pragma unroll
-                            for (int t = 0; t < 4; ++t)
-                                v[t] = STAGE == kStageB ? cb * ov[t] + cc * v[t] : ca * ov[t] + v[t];
+                            for (int t = 0; t < 4; ++t) w[t] = ca * ov[t] + w[t];
+                        } else {
+                            if (STAGE == kStageB) {
+                                decode4(raw[j][g], ov);
+#pragma unroll
+                                for (int t = 0; t < 4; ++t) v[t] = cb * ov[t] + cc * v[t];
+                            }
+                            if (write_t) store4(out_t + int64_t(gj) * rp + gi, v);
+                            quad_transpose(v, w, s4);
                         }
-                        if (write_t) store4(out_t + int64_t(gj) * ld_t + gi, v);
-                        float w[4];
-                        quad_transpose(v, w, s4);
                         store4(out_n + int64_t(gi + s4) * ld_n + (gj - s4), w);
                     }
                 }
             }
         }
     } else {
-        // Last iteration: O = fl(s * X) in the matrix's own R x C layout.
-        const TE* xt = static_cast<const TE*>(args.xt_cur) + mt.x_off;
+        // Last iteration: O = fl(s * (a X + B X)) in the matrix's own R x C layout.
         float* om = args.o + mt.off;
         const float sc = mt.scale;
         const int r = mt.r, c = mt.c;
@@ -482,8 +590,7 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
 #pragma unroll
             for (int j = 0; j < kNj; ++j)
 #pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    raw[j][g] = load_raw4(xt + int64_t(col0 + j * 32) * rp + row0 + i * 32 + g * 8);
+                for (int g = 0; g < 4; ++g) raw[j][g] = load_raw4(x_row(i, j, g));
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int j = 0; j < kNj; ++j) {
@@ -491,12 +598,14 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                 for (int g = 0; g < 4; ++g) {
                     const int gi = row0 + i * 32 + g * 8;
                     const int gj = col0 + j * 32;
-                    float v[4], xv[4];
-                    decode4(raw[j][g], xv);
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) v[t] = sc * (ca * xv[t] + acc[i][j][g * 4 + t]);
+                    float v[4], xv[4], w[4];
+                    decode4(raw[j][g], xv);  // row layout
                     if (tall) {
-                        // O is c x r: O[gj][gi + t], 4 consecutive elements
+                        // O is c x r: O[gj][gi + t] = X[gi + t][gj], column layout
+                        float xcol[4];
+                        quad_transpose(xv, xcol, s4);
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) v[t] = sc * (ca * xcol[t] + acc[i][j][g * 4 + t]);
                         if (gj < c) {
                             float* dst = om + int64_t(gj) * r + gi;
                             if (gi + 3 < r && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
@@ -508,9 +617,12 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                             }
                         }
                     } else {
-                        // O is r x c: after the quad exchange, O[gi + s][gj - s + t]
-                        float w[4];
+                        // O is r x c: in the row layout, O[gi + s][gj - s + t]
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) v[t] = acc[i][j][g * 4 + t];
                         quad_transpose(v, w, s4);
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) w[t] = sc * (ca * xv[t] + w[t]);
                         const int orow = gi + s4, ocol = gj - s4;
                         if (orow < r) {
                             float* dst = om + int64_t(orow) * c + ocol;
@@ -575,9 +687,8 @@ hipError_t launch_newton_schulz(const PlanView& p, void* ws, float* o, int ns_st
     for (int it = 0; it < ns_steps; ++it) {
         NsArgs a{};
         a.mats = p.mats;
-        a.x = w + p.ws.x;
-        a.xt_cur = w + p.ws.xt[it & 1];
-        a.xt_next = w + p.ws.xt[(it + 1) & 1];
+        a.x_cur = w + p.ws.x[it & 1];
+        a.x_next = w + p.ws.x[(it + 1) & 1];
         a.ga = w + p.ws.a;
         a.gb = w + p.ws.b;
         a.o = o;

@@ -50,8 +50,7 @@ struct alignas(16) MatInfo {
     int64_t poff;       // start of slice 0 in params
     int64_t pstride;    // slice stride in params
     int64_t slice_len;  // numel / n_shards
-    int64_t x_off;      // start of X (rp x cp) in the X region; X^T (cp x rp) at the same
-                        // offset in each X^T region
+    int64_t x_off;      // start of X (rp x cp) in each of the two X regions
     int64_t g_off;      // start of the rp x rp Gram block in the A and B regions
     int32_t R, C;       // original shape
     int32_t r, c;       // NS-orientation shape
@@ -73,8 +72,7 @@ struct alignas(16) GemmTile {
 // Byte offsets of the workspace regions.
 struct WsLayout {
     size_t u;        // float32 U / O, laid out like grads (state extent E)
-    size_t x;        // X, rp x cp per matrix
-    size_t xt[2];    // X^T ping-pong, cp x rp per matrix
+    size_t x[2];     // X ping-pong (iteration input / output), rp x cp per matrix
     size_t a, b;     // Gram matrices rp x rp per matrix
     size_t partial;  // one float per elementwise chunk
     size_t inv;      // one float per matrix
@@ -173,8 +171,9 @@ hipError_t launch_front(const PlanView& p, const float* grads, float* momentum, 
 hipError_t launch_sumsq(const PlanView& p, const float* u, float* partial, hipStream_t s);
 // Per-matrix 1 / (sqrt(sum of partials) + eps).
 hipError_t launch_norm(const PlanView& p, const float* partial, float* inv, hipStream_t s);
-// X0 = cast(U * inv) in NS orientation (and X0^T), zero padding; when
-// o_direct is non-null (ns_steps == 0) write O = s * X0 there instead.
+// X0 = cast(U * inv) in NS orientation into the first X region, zero
+// padding; when o_direct is non-null (ns_steps == 0) write O = s * X0 there
+// instead.
 hipError_t launch_cast(const PlanView& p, const float* u, const float* inv, void* ws,
                        float* o_direct, hipStream_t s);
 // ns_steps >= 1 Newton-Schulz iterations; the last writes O = s * X in the

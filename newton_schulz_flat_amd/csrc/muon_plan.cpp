@@ -95,11 +95,11 @@ Geometry build_geometry(const muon_matrix_desc_t* d, int64_t n, int gemm_mode) {
     size_t at = 0;
     w.u = at;
     at = align_up(at + size_t(g.state_extent) * 4, kWsAlign);
-    w.x = at;
-    at = align_up(at + size_t(x_elems) * es, kWsAlign);
-    w.xt[0] = at;
-    at = align_up(at + size_t(x_elems) * es, kWsAlign);
-    w.xt[1] = at;
+    // The second X region starts 64 KiB past an alignment boundary so that the
+    // two iterates never alias at a power-of-two distance.
+    w.x[0] = at;
+    at = align_up(at + size_t(x_elems) * es, kWsAlign) + (size_t(1) << 16);
+    w.x[1] = at;
     at = align_up(at + size_t(x_elems) * es, kWsAlign);
     w.a = at;
     at = align_up(at + size_t(g_elems) * es, kWsAlign);
