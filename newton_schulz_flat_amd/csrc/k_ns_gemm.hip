@@ -153,8 +153,23 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-// Two transposing LDS reads (ds_read_b64_tr_b16) at p and p + second, as one
-// 8-element MFMA operand.  p points into LDS.
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane g points at 4 consecutive 16-bit elements of row (g >> 2) of a 4 x 16
+// block, at column 4 (g & 3); it receives column g of the block, i.e. the
+// elements of rows 0..3 at column g.  p points into LDS.
+__device__ __forceinline__ uint2 read_tr1(const unsigned char* p) {
+    return __builtin_bit_cast(
+        uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(const_cast<unsigned char*>(p))));
+}
+
+// Two float32 values rounded to bfloat16 (nearest even) and packed, low first.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two transposing LDS reads at p and p + second, as one 8-element MFMA operand.
 __device__ __forceinline__ u32x4 read_tr(const unsigned char* p, int second) {
     const uint2 lo = __builtin_bit_cast(
         uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(const_cast<unsigned char*>(p))));
@@ -295,6 +310,24 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+    // Main loop.  A K block is consumed in four steps q of 16 bf16 (4 float32)
+    // per lane; its instruction order is fixed with scheduling barriers so
+    // that each MFMA is followed by at most a few memory instructions:
+    //   q = 0, 1, 2: fragments of step q+1 are read from LDS (double-buffered
+    //                registers);
+    //   q = 2:       the next block, already in registers, is written to the
+    //                other LDS buffer, then all waves meet at the barrier;
+    //   q = 3:       the MFMAs run on fragments already in registers while the
+    //                fragments of step 0 of the next block are read and the
+    //                global loads of the block after it are issued.
+    // Keeping step 3's MFMAs behind the barrier gives the matrix pipe work while
+    // every wave refills its fragments.  Blocks past the end reload the last
+    // block (valid, unused copies) so the loop stays branch free.
+    const int nkb = K / kBk;
+    constexpr int kMfma = kMi * kNj;  // MFMAs per step q (per K sub-step for bf16)
+    auto q_off = [&](int blk) -> int64_t {
+        return (kTransQ || kQLdsT) ? int64_t(blk) * kBk * cp : int64_t(blk) * kBk;
+    };
     u32x4 pa[kL], pb[kL];
 #pragma unroll
     for (int l = 0; l < kL; ++l) {
@@ -305,18 +338,16 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
     for (int l = 0; l < kL; ++l) *reinterpret_cast<u32x4*>(lds + lds_st + l * kLdsPass) = pa[l];
 #pragma unroll
     for (int w = 0; w < kQW; ++w) store_q<kTransQ, kL>(lds + q_st, pb, w, q_pass);
+    {
+        const int b1 = nkb > 1 ? 1 : 0;
+#pragma unroll
+        for (int l = 0; l < kL; ++l) {
+            pa[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep + int64_t(b1) * kBk);
+            pb[l] = *reinterpret_cast<const u32x4*>(gq + l * qstep + q_off(b1));
+        }
+    }
     __syncthreads();
 
-    // Main loop.  One K block is a single basic block whose instruction order
-    // is fixed with scheduling barriers: each MFMA is followed by at most a few
-    // memory instructions, so the matrix pipe keeps issuing while
-    //   q = 0: the 2*kL global loads of the next block are issued,
-    //   q < 3: the fragments of step q+1 are read from LDS (double-buffered
-    //          registers),
-    //   q = 3: the prefetched block is written to the other LDS buffer.
-    // The last block reloads itself (a valid, unused copy) to stay branch free.
-    const int nkb = K / kBk;
-    constexpr int kMfma = kMi * kNj;  // MFMAs per step q (per K sub-step for bf16)
     u32x4 fa[2][kMi], fb[2][kNj];
 #pragma unroll
     for (int i = 0; i < kMi; ++i)
@@ -326,13 +357,16 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
         fb[0][j] = kQLdsT ? read_tr(lds + fbt_off + j * 64, 4 * kS)
                           : *reinterpret_cast<const u32x4*>(lds + fb_off + j * 32 * kLdsStride);
     for (int kb = 0; kb < nkb; ++kb) {
-        const int64_t k0 = int64_t(kb + 1 < nkb ? kb + 1 : kb) * kBk;
-        const int64_t qk = (kTransQ || kQLdsT) ? k0 * cp : k0;  // Q offset of the next block
+        const int b2 = kb + 2 < nkb ? kb + 2 : nkb - 1;  // block loaded during step 3
+        const int64_t k2 = int64_t(b2) * kBk, qk2 = q_off(b2);
         const unsigned char* buf = lds + (kb & 1) * kBuf;
         unsigned char* nbuf = lds + ((kb + 1) & 1) * kBuf;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int cur = q & 1;
+            // fragments read during this step: step q+1 of this block, or step 0 of the next
+            const unsigned char* rbuf = q < 3 ? buf : nbuf;
+            const int rq = q < 3 ? q + 1 : 0;
 #pragma unroll
             for (int m = 0; m < kMfma; ++m) {
                 const int i = m / kNj, j = m % kNj;
@@ -347,31 +381,19 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                             __uint_as_float(fa[cur][i][e]), __uint_as_float(fb[cur][j][e]), acc[i][j],
                             0, 0, 0);
                 }
-                if (q < 3) {
 #pragma unroll
-                    for (int rd = m; rd < kMi + kNj; rd += kMfma) {
-                        const int at = (q + 1) * 16;
-                        if (rd < kMi)
-                            fa[cur ^ 1][rd] = *reinterpret_cast<const u32x4*>(
-                                buf + fa_off + rd * 32 * kLdsStride + at);
-                        else if (kQLdsT)
-                            fb[cur ^ 1][rd - kMi] =
-                                read_tr(buf + fbt_off + (rd - kMi) * 64 + (q + 1) * 8 * kS, 4 * kS);
-                        else
-                            fb[cur ^ 1][rd - kMi] = *reinterpret_cast<const u32x4*>(
-                                buf + fb_off + (rd - kMi) * 32 * kLdsStride + at);
-                    }
+                for (int rd = m; rd < kMi + kNj; rd += kMfma) {
+                    if (rd < kMi)
+                        fa[cur ^ 1][rd] = *reinterpret_cast<const u32x4*>(
+                            rbuf + fa_off + rd * 32 * kLdsStride + rq * 16);
+                    else if (kQLdsT)
+                        fb[cur ^ 1][rd - kMi] =
+                            read_tr(rbuf + fbt_off + (rd - kMi) * 64 + rq * 8 * kS, 4 * kS);
+                    else
+                        fb[cur ^ 1][rd - kMi] = *reinterpret_cast<const u32x4*>(
+                            rbuf + fb_off + (rd - kMi) * 32 * kLdsStride + rq * 16);
                 }
-                if (q == 0) {
-#pragma unroll
-                    for (int l = m; l < 2 * kL; l += kMfma) {
-                        if (l < kL)
-                            pa[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep + k0);
-                        else
-                            pb[l - kL] = *reinterpret_cast<const u32x4*>(gq + (l - kL) * qstep + qk);
-                    }
-                }
-                if (q == 3) {
+                if (q == 2) {
 #pragma unroll
                     for (int l = m; l < kL + kQW; l += kMfma) {
                         if (l < kL)
@@ -380,19 +402,23 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                             store_q<kTransQ, kL>(nbuf + q_st, pb, l - kL, q_pass);
                     }
                 }
+                if (q == 3) {
+#pragma unroll
+                    for (int l = m; l < 2 * kL; l += kMfma) {
+                        if (l < kL)
+                            pa[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep + k2);
+                        else
+                            pb[l - kL] = *reinterpret_cast<const u32x4*>(gq + (l - kL) * qstep + qk2);
+                    }
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
+            if (q == 2) __syncthreads();
         }
-        __syncthreads();
-        // fragments of step 0 of the next block
-#pragma unroll
-        for (int i = 0; i < kMi; ++i)
-            fa[0][i] = *reinterpret_cast<const u32x4*>(nbuf + fa_off + i * 32 * kLdsStride);
-#pragma unroll
-        for (int j = 0; j < kNj; ++j)
-            fb[0][j] = kQLdsT ? read_tr(nbuf + fbt_off + j * 64, 4 * kS)
-                              : *reinterpret_cast<const u32x4*>(nbuf + fb_off + j * 32 * kLdsStride);
     }
+    // the last step read (unused) fragments: let every wave finish with LDS
+    // before the epilogue reuses it
+    __syncthreads();
 
     // Epilogue.  Lane (lr, hk) of fragment (i, j) holds, for g = 0..3, the
     // outputs at rows gi + 0..3 (gi = wave row + i*32 + g*8 + hk*4) of column gj
@@ -425,117 +451,106 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
         // stage-B operand A, read along a column (A is symmetric)
         const TE* ga = static_cast<const TE*>(args.ga) + mt.g_off;
         if constexpr (BF16) {
-            // bfloat16 outputs go through LDS so that every global store writes
-            // 16 contiguous bytes per lane along an output row.  Each wave stages its
-            // own kWm x kWn sub-tile (rows padded by 16 bytes) in a private region:
-            // for a mirrored tile first in the column layout (for out_t), then in
-            // the row layout (for out_n).  The values are rounded to bfloat16 once
-            // and kept packed in registers between the two passes (in the row
-            // layout already for stage X).  The main loop ended with a barrier, so
-            // LDS is free.
+            // bfloat16 tiles go through a wave-private LDS region in three passes,
+            // so that every global access is a 16-byte run along a row:
+            //  1. (stages B, X) the operand sub-tile is loaded along its rows and
+            //     staged row-major; transposing reads then hand each lane the 4
+            //     rows x 1 column it holds in the accumulators;
+            //  2. the rounded results are staged column-major (staged row = output
+            //     column), which a mirrored tile stores as it is;
+            //  3. transposing reads of the column-major staging return output rows
+            //     for the row-oriented stores.
+            // The main loop ended with a barrier, so LDS is free.
             constexpr int kWm = G::kWm, kWn = G::kWn;
-            constexpr int kStrideT = kWm * 2 + 16;  // column-oriented: kWn rows of kWm
-            constexpr int kStrideN = kWn * 2 + 16;  // row-oriented: kWm rows of kWn
-            constexpr int kRegion = (kWn * kStrideT > kWm * kStrideN) ? kWn * kStrideT : kWm * kStrideN;
+            constexpr int kStrideT = kWm * 2 + 16;  // column-major staging: kWn rows of kWm
+            constexpr int kStrideO = kWn * 2 + 16;  // operand staging: kWm rows of kWn
+            constexpr int kRegion = (kWn * kStrideT > kWm * kStrideO) ? kWn * kStrideT : kWm * kStrideO;
             static_assert(kRegion * G::kWaves <= 2 * kBuf, "epilogue staging exceeds LDS");
             unsigned char* wl = lds + wave * kRegion;
+            const int r0w = ti * TILE + wm * kWm, c0w = tj * TILE + wn * kWn;  // wave sub-tile origin
+            // transposing-read lane geometry (see read_tr): row (g >> 2), column 4 (g & 3)
+            const int tr_r = (lane & 15) >> 2, tr_c = (lane & 3) * 4;
             uint32_t pk[kMi][kNj][4][2];
-            constexpr int kIB = kMi > 1 ? kMi / 2 : 1;  // fragment rows per load batch
+            if (STAGE != kStageA) {
+                const int old = STAGE == kStageB ? rp : cp;
+                const TE* src = (STAGE == kStageB ? ga + int64_t(r0w) * rp : xc + int64_t(r0w) * cp) + c0w;
+                constexpr int kCpr = kWn / 8;             // 16-byte chunks per operand row
+                constexpr int kChunks = kWm * kCpr / 64;  // per lane
+                u32x4 ov[kChunks];
 #pragma unroll
-            for (int i0 = 0; i0 < kMi; i0 += kIB) {
-                Raw4<TE> raw[kIB][kNj][4];
-                if (STAGE != kStageA) {
-#pragma unroll
-                    for (int ii = 0; ii < kIB; ++ii)
-#pragma unroll
-                        for (int j = 0; j < kNj; ++j)
-#pragma unroll
-                            for (int g = 0; g < 4; ++g)
-                                raw[ii][j][g] = STAGE == kStageX
-                                                    ? load_raw4(x_row(i0 + ii, j, g))
-                                                    : load_raw4(ga + int64_t(col0 + j * 32) * rp + row0 +
-                                                                (i0 + ii) * 32 + g * 8);
+                for (int t = 0; t < kChunks; ++t) {
+                    const int ch = t * 64 + lane, r = ch / kCpr, c16 = ch % kCpr;
+                    ov[t] = *reinterpret_cast<const u32x4*>(src + int64_t(r) * old + c16 * 8);
                 }
-                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int ii = 0; ii < kIB; ++ii) {
-                    const int i = i0 + ii;
-#pragma unroll
-                    for (int j = 0; j < kNj; ++j) {
-#pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-                            float v[4];
-#pragma unroll
-                            for (int t = 0; t < 4; ++t) v[t] = acc[i][j][g * 4 + t];
-                            if (STAGE == kStageX) {
-                                float w[4], ov[4];
-                                quad_transpose(v, w, s4);
-                                decode4(raw[ii][j][g], ov);
-#pragma unroll
-                                for (int t = 0; t < 4; ++t) v[t] = ca * ov[t] + w[t];
-                            } else if (STAGE == kStageB) {
-                                float ov[4];
-                                decode4(raw[ii][j][g], ov);
-#pragma unroll
-                                for (int t = 0; t < 4; ++t) v[t] = cb * ov[t] + cc * v[t];
-                            }
-                            pk[i][j][g][0] = uint32_t(bf16_rne(v[0])) | (uint32_t(bf16_rne(v[1])) << 16);
-                            pk[i][j][g][1] = uint32_t(bf16_rne(v[2])) | (uint32_t(bf16_rne(v[3])) << 16);
-                        }
-                    }
-                }
-            }
-            // staged row r (cols elements each, stride bytes apart) -> global row
-            // base_r + r, columns base_c ..
-            auto drain = [&](TE* out, int ldo, int base_r, int base_c, int cols, int stride,
-                             int rows) {
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                const int cpr = cols / 8;  // 16-byte chunks per staged row
-                const int chunks = rows * cpr / 64;
-                for (int t = 0; t < chunks; ++t) {
-                    const int ch = t * 64 + lane;
-                    const int r = ch / cpr, c16 = ch % cpr;
-                    const u32x4 val = *reinterpret_cast<const u32x4*>(wl + r * stride + c16 * 16);
-                    *reinterpret_cast<u32x4*>(out + int64_t(base_r + r) * ldo + base_c + c16 * 8) = val;
+                for (int t = 0; t < kChunks; ++t) {
+                    const int ch = t * 64 + lane, r = ch / kCpr, c16 = ch % kCpr;
+                    *reinterpret_cast<u32x4*>(wl + r * kStrideO + c16 * 16) = ov[t];
                 }
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            };
-            if (write_t) {
-                // column layout: staged row = output column j*32 + lr, 4 rows per lane
 #pragma unroll
                 for (int i = 0; i < kMi; ++i)
 #pragma unroll
                     for (int j = 0; j < kNj; ++j)
 #pragma unroll
                         for (int g = 0; g < 4; ++g) {
-                            const int sr = j * 32 + lr, sc = i * 32 + g * 8 + hk * 4;
-                            *reinterpret_cast<uint2*>(wl + sr * kStrideT + sc * 2) =
-                                make_uint2(pk[i][j][g][0], pk[i][j][g][1]);
+                            // rows i*32 + g*8 + hk*4 + 0..3, column j*32 + lr of the sub-tile
+                            const uint2 x2 = read_tr1(wl + (i * 32 + g * 8 + hk * 4 + tr_r) * kStrideO +
+                                                      (j * 32 + (lane & 16) + tr_c) * 2);
+                            float ov4[4] = {__uint_as_float(x2.x << 16), __uint_as_float(x2.x & 0xffff0000u),
+                                            __uint_as_float(x2.y << 16), __uint_as_float(x2.y & 0xffff0000u)};
+                            float v[4];
+#pragma unroll
+                            for (int t = 0; t < 4; ++t)
+                                v[t] = STAGE == kStageB ? cb * ov4[t] + cc * acc[i][j][g * 4 + t]
+                                                        : ca * ov4[t] + acc[i][j][g * 4 + t];
+                            pk[i][j][g][0] = pack_bf16(v[0], v[1]);
+                            pk[i][j][g][1] = pack_bf16(v[2], v[3]);
                         }
-                drain(out_t, rp, tj * TILE + wn * kWn, ti * TILE + wm * kWm, kWm, kStrideT, kWn);
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            } else {
+#pragma unroll
+                for (int i = 0; i < kMi; ++i)
+#pragma unroll
+                    for (int j = 0; j < kNj; ++j)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            pk[i][j][g][0] = pack_bf16(acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1]);
+                            pk[i][j][g][1] = pack_bf16(acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]);
+                        }
             }
-            // row layout: lane s holds row (.. + s), columns c - s ..
+            // column-major staging: staged row = output column j*32 + lr, 4 rows per lane
 #pragma unroll
             for (int i = 0; i < kMi; ++i)
 #pragma unroll
                 for (int j = 0; j < kNj; ++j)
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
-                        uint32_t lo = pk[i][j][g][0], hi = pk[i][j][g][1];
-                        if (STAGE != kStageX) {
-                            float v[4], w[4];
-                            v[0] = __uint_as_float(lo << 16);
-                            v[1] = __uint_as_float(lo & 0xffff0000u);
-                            v[2] = __uint_as_float(hi << 16);
-                            v[3] = __uint_as_float(hi & 0xffff0000u);
-                            quad_transpose(v, w, s4);
-                            lo = (__float_as_uint(w[0]) >> 16) | (__float_as_uint(w[1]) & 0xffff0000u);
-                            hi = (__float_as_uint(w[2]) >> 16) | (__float_as_uint(w[3]) & 0xffff0000u);
-                        }
-                        const int sr = i * 32 + g * 8 + hk * 4 + s4, sc = j * 32 + lr - s4;
-                        *reinterpret_cast<uint2*>(wl + sr * kStrideN + sc * 2) = make_uint2(lo, hi);
+                        const int sr = j * 32 + lr, sc = i * 32 + g * 8 + hk * 4;
+                        *reinterpret_cast<uint2*>(wl + sr * kStrideT + sc * 2) =
+                            make_uint2(pk[i][j][g][0], pk[i][j][g][1]);
                     }
-            drain(out_n, ld_n, ti * TILE + wm * kWm, tj * TILE + wn * kWn, kWn, kStrideN, kWm);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (write_t) {
+                // mirror tile: staged row c -> global row c0w + c of out_t, columns r0w ..
+                constexpr int cpr = kWm / 8;
+#pragma unroll 4
+                for (int t = 0; t < kWn * cpr / 64; ++t) {
+                    const int ch = t * 64 + lane, r = ch / cpr, c16 = ch % cpr;
+                    const u32x4 val = *reinterpret_cast<const u32x4*>(wl + r * kStrideT + c16 * 16);
+                    *reinterpret_cast<u32x4*>(out_t + int64_t(c0w + r) * rp + r0w + c16 * 8) = val;
+                }
+            }
+            // row-oriented stores: per pass, 16-lane group G takes output rows
+            // rb + 0..15 (lane g: row rb + g) and columns cb + 8G .. cb + 8G + 7,
+            // read as staged rows cb + 8G + 0..3 and + 4..7 at staged column rb + 4 (g & 3)
+#pragma unroll 4
+            for (int t = 0; t < (kWm / 16) * (kWn / 32); ++t) {
+                const int rb = (t % (kWm / 16)) * 16, cb = (t / (kWm / 16)) * 32 + (lane >> 4) * 8;
+                const unsigned char* p = wl + (cb + tr_r) * kStrideT + (rb + tr_c) * 2;
+                const u32x4 val = read_tr(p, 4 * kStrideT);
+                *reinterpret_cast<u32x4*>(out_n + int64_t(r0w + rb + (lane & 15)) * ld_n + c0w + cb) = val;
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < kMi; ++i) {
