@@ -56,6 +56,10 @@ struct NsArgs {
     float* o;       // O (last iteration), laid out like the gradients
     float ca, cb, cc;
     int last;
+    // fused apply on the last iteration (fuse != 0): W <- fl(fl(W decay) - fl(lr O))
+    void* params;
+    float decay, lr;
+    int fuse, param_bf16;
 };
 
 constexpr int kRowBytes = 128;  // K block: bytes of one operand row
@@ -167,6 +171,70 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
     return __builtin_bit_cast(uint32_t, v);
+}
+
+// W <- fl(fl(W decay) - fl(lr O)) for elements e .. e + cnt - 1 (cnt <= 4) of a
+// matrix in its own row-major order, each written to its shard slice: the
+// decay-and-update of the apply phase, with the same three roundings and the
+// same round-to-nearest-even store, applied where O is produced.
+__device__ __forceinline__ void load_w4(const float* p, float w[4]) {
+    const float4 t = *reinterpret_cast<const float4*>(p);
+    w[0] = t.x, w[1] = t.y, w[2] = t.z, w[3] = t.w;
+}
+__device__ __forceinline__ void load_w4(const uint16_t* p, float w[4]) {
+    const uint2 t = *reinterpret_cast<const uint2*>(p);
+    w[0] = __uint_as_float(t.x << 16), w[1] = __uint_as_float(t.x & 0xffff0000u);
+    w[2] = __uint_as_float(t.y << 16), w[3] = __uint_as_float(t.y & 0xffff0000u);
+}
+__device__ __forceinline__ void store_w4(float* p, const float r[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(r[0], r[1], r[2], r[3]);
+}
+__device__ __forceinline__ void store_w4(uint16_t* p, const float r[4]) {
+    const uint32_t lo = uint32_t(bf16_rne(r[0])) | (uint32_t(bf16_rne(r[1])) << 16);
+    const uint32_t hi = uint32_t(bf16_rne(r[2])) | (uint32_t(bf16_rne(r[3])) << 16);
+    *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+}
+__device__ __forceinline__ float load_w1(const float* p) { return *p; }
+__device__ __forceinline__ float load_w1(const uint16_t* p) { return __uint_as_float(uint32_t(*p) << 16); }
+__device__ __forceinline__ void store_w1(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_w1(uint16_t* p, float v) { *p = bf16_rne(v); }
+
+template <typename TW>
+__device__ __forceinline__ void apply_span(TW* __restrict__ params, const MatInfo& mt, int64_t e,
+                                           int cnt, const float o[4], float decay, float lr) {
+#pragma clang fp contract(off)
+    const int64_t slice = mt.slice_len;
+    const bool sharded = slice != mt.numel;
+    if (cnt == 4 && (e & 3) == 0) {
+        // sharded slices are multiples of 8 long: an aligned group of 4 never straddles two
+        int64_t dst = mt.poff + e;
+        if (sharded) {
+            const int64_t k = e / slice;
+            dst = mt.poff + k * mt.pstride + (e - k * slice);
+        }
+        float w[4], r[4];
+        load_w4(params + dst, w);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float w1 = w[t] * decay;
+            const float u = lr * o[t];
+            r[t] = w1 - u;
+        }
+        store_w4(params + dst, r);
+    } else {
+        // static indexing only: o[] must stay in registers
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            if (t < cnt) {
+                const int64_t j = e + t;
+                const int64_t k = sharded ? j / slice : 0;
+                TW* dst = params + mt.poff + k * mt.pstride + (j - k * slice);
+                const float w1 = load_w1(dst) * decay;
+                const float u = lr * o[t];
+                store_w1(dst, w1 - u);
+            }
+        }
+    }
 }
 
 // Two transposing LDS reads at p and p + second, as one 8-element MFMA operand.
@@ -594,11 +662,22 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
             }
         }
     } else {
-        // Last iteration: O = fl(s * (a X + B X)) in the matrix's own R x C layout.
+        // Last iteration: O = fl(s * (a X + B X)) in the matrix's own R x C layout,
+        // stored, or (fused apply) used at once to update the weights.  Each
+        // 32-row band of the wave's sub-tile is staged in a wave-private LDS region
+        // in O's own orientation, then written out along O's rows.
         float* om = args.o + mt.off;
         const float sc = mt.scale;
         const int r = mt.r, c = mt.c;
         const bool tall = mt.tall != 0;
+        const int rows_o = tall ? c : r, cols_o = tall ? r : c;  // O's shape
+        constexpr int kWn = G::kWn;
+        constexpr int kPN = kWn + 4;  // float pitch, wide: 32 O rows of kWn
+        constexpr int kPT = 32 + 4;   // float pitch, tall: kWn O rows of 32
+        constexpr int kRegionL = (32 * kPN > kWn * kPT ? 32 * kPN : kWn * kPT) * 4;
+        static_assert(kRegionL * G::kWaves <= 2 * kBuf, "epilogue staging exceeds LDS");
+        float* wl = reinterpret_cast<float*>(lds + wave * kRegionL);
+        const int r0w = ti * TILE + wm * G::kWm, c0w = tj * TILE + wn * kWn;
 #pragma unroll
         for (int i = 0; i < kMi; ++i) {
             Raw4<TE> raw[kNj][4];
@@ -607,48 +686,58 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
 #pragma unroll
                 for (int g = 0; g < 4; ++g) raw[j][g] = load_raw4(x_row(i, j, g));
             __builtin_amdgcn_sched_barrier(0);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // previous band read back
 #pragma unroll
             for (int j = 0; j < kNj; ++j) {
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int gi = row0 + i * 32 + g * 8;
-                    const int gj = col0 + j * 32;
                     float v[4], xv[4], w[4];
                     decode4(raw[j][g], xv);  // row layout
                     if (tall) {
-                        // O is c x r: O[gj][gi + t] = X[gi + t][gj], column layout
+                        // O[gj][gi + t] = X[gi + t][gj]: the column layout, 4 consecutive O elements
                         float xcol[4];
                         quad_transpose(xv, xcol, s4);
 #pragma unroll
                         for (int t = 0; t < 4; ++t) v[t] = sc * (ca * xcol[t] + acc[i][j][g * 4 + t]);
-                        if (gj < c) {
-                            float* dst = om + int64_t(gj) * r + gi;
-                            if (gi + 3 < r && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-                                store4(dst, v);
-                            } else {
-#pragma unroll
-                                for (int t = 0; t < 4; ++t)
-                                    if (gi + t < r) dst[t] = v[t];
-                            }
-                        }
+                        *reinterpret_cast<float4*>(wl + (j * 32 + lr) * kPT + g * 8 + (lane >> 5) * 4) =
+                            make_float4(v[0], v[1], v[2], v[3]);
                     } else {
-                        // O is r x c: in the row layout, O[gi + s][gj - s + t]
+                        // O[gi + s][gj - s + t]: the row layout after the quad exchange
 #pragma unroll
                         for (int t = 0; t < 4; ++t) v[t] = acc[i][j][g * 4 + t];
                         quad_transpose(v, w, s4);
 #pragma unroll
                         for (int t = 0; t < 4; ++t) w[t] = sc * (ca * xv[t] + w[t]);
-                        const int orow = gi + s4, ocol = gj - s4;
-                        if (orow < r) {
-                            float* dst = om + int64_t(orow) * c + ocol;
-                            if (ocol + 3 < c && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-                                store4(dst, w);
-                            } else {
+                        *reinterpret_cast<float4*>(wl + (g * 8 + (lane >> 5) * 4 + s4) * kPN + j * 32 + lr - s4) =
+                            make_float4(w[0], w[1], w[2], w[3]);
+                    }
+                }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            // the band is 32 x kWn (wide) or kWn x 32 (tall) O elements; 4 per lane per pass
+            const int cpr = tall ? 8 : kWn / 4;  // 4-element chunks per staged row
+            const int pitch = tall ? kPT : kPN;
+            const int a0 = tall ? c0w : r0w + i * 32, b0 = tall ? r0w + i * 32 : c0w;
+#pragma unroll 2
+            for (int t = 0; t < 32 * kWn / 4 / 64; ++t) {
+                const int ch = t * 64 + lane, lrow = ch / cpr, lc = (ch % cpr) * 4;
+                const int a = a0 + lrow, b = b0 + lc;
+                if (a < rows_o && b < cols_o) {
+                    const float4 q = *reinterpret_cast<const float4*>(wl + lrow * pitch + lc);
+                    const float ov[4] = {q.x, q.y, q.z, q.w};
+                    const int cnt = b + 3 < cols_o ? 4 : cols_o - b;
+                    const int64_t e = int64_t(a) * cols_o + b;
+                    if (args.fuse) {
+                        if (args.param_bf16)
+                            apply_span(static_cast<uint16_t*>(args.params), mt, e, cnt, ov, args.decay, args.lr);
+                        else
+                            apply_span(static_cast<float*>(args.params), mt, e, cnt, ov, args.decay, args.lr);
+                    } else if (cnt == 4 && (e & 3) == 0) {
+                        store4(om + e, ov);
+                    } else {
 #pragma unroll
-                                for (int t = 0; t < 4; ++t)
-                                    if (ocol + t < c) dst[t] = w[t];
-                            }
-                        }
+                        for (int u = 0; u < 4; ++u)
+                            if (u < cnt) om[e + u] = ov[u];
                     }
                 }
             }
@@ -695,8 +784,8 @@ hipError_t launch_class(int tile, int stage, int n_tiles, const NsArgs& a, hipSt
 
 }  // namespace
 
-hipError_t launch_newton_schulz(const PlanView& p, void* ws, float* o, int ns_steps,
-                                hipStream_t s) {
+hipError_t launch_newton_schulz(const PlanView& p, void* ws, float* o, const FusedApply* fuse,
+                                int ns_steps, hipStream_t s) {
     unsigned char* w = static_cast<unsigned char*>(ws);
     const bool bf16 = p.gemm_mode != MUON_GEMM_F32;
     for (int it = 0; it < ns_steps; ++it) {
@@ -711,6 +800,13 @@ hipError_t launch_newton_schulz(const PlanView& p, void* ws, float* o, int ns_st
         a.cb = kNsB;
         a.cc = kNsC;
         a.last = it == ns_steps - 1;
+        if (fuse && a.last) {
+            a.params = fuse->params;
+            a.decay = fuse->decay;
+            a.lr = fuse->lr;
+            a.fuse = 1;
+            a.param_bf16 = fuse->param_dtype == MUON_DTYPE_BF16;
+        }
         for (int stage = kStageA; stage <= kStageX; ++stage) {
             for (int c = 0; c < p.n_classes; ++c) {
                 const TileClassDev& tc = p.classes[c];

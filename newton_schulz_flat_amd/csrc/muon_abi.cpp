@@ -155,9 +155,13 @@ int muon_step(void* params, int param_dtype, int64_t n_param_elems, const float*
     TRY_HIP(muon::launch_front(p, grads, momentum, u, partial, beta, nesterov, stream), "front");
     TRY_HIP(muon::launch_norm(p, partial, inv, stream), "norm");
     TRY_HIP(muon::launch_cast(p, u, inv, ws, ns_steps == 0 ? u : nullptr, stream), "cast");
-    if (ns_steps > 0)
-        TRY_HIP(muon::launch_newton_schulz(p, ws, u, ns_steps, stream), "newton-schulz");
-    TRY_HIP(muon::launch_apply(p, params, param_dtype, u, decay, lr, stream), "apply");
+    if (ns_steps > 0) {
+        // the last iteration applies the update itself (same roundings as the apply phase)
+        const muon::FusedApply fuse{params, param_dtype, decay, lr};
+        TRY_HIP(muon::launch_newton_schulz(p, ws, u, &fuse, ns_steps, stream), "newton-schulz");
+    } else {
+        TRY_HIP(muon::launch_apply(p, params, param_dtype, u, decay, lr, stream), "apply");
+    }
     return MUON_OK;
 }
 
@@ -213,7 +217,7 @@ int muon_orthogonalize(const float* u, float* o_out, int64_t n_elems,
     TRY_HIP(muon::launch_norm(p, partial, inv, stream), "norm");
     TRY_HIP(muon::launch_cast(p, u, inv, ws, ns_steps == 0 ? o_out : nullptr, stream), "cast");
     if (ns_steps > 0)
-        TRY_HIP(muon::launch_newton_schulz(p, ws, o_out, ns_steps, stream), "newton-schulz");
+        TRY_HIP(muon::launch_newton_schulz(p, ws, o_out, nullptr, ns_steps, stream), "newton-schulz");
     return MUON_OK;
 }
 

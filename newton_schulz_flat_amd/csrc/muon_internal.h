@@ -176,10 +176,18 @@ hipError_t launch_norm(const PlanView& p, const float* partial, float* inv, hipS
 // instead.
 hipError_t launch_cast(const PlanView& p, const float* u, const float* inv, void* ws,
                        float* o_direct, hipStream_t s);
+// The decay-and-update of the apply phase, for the last Newton-Schulz
+// iteration to perform in place of storing O.
+struct FusedApply {
+    void* params;
+    int param_dtype;
+    float decay, lr;
+};
 // ns_steps >= 1 Newton-Schulz iterations; the last writes O = s * X in the
-// original orientation to o.
-hipError_t launch_newton_schulz(const PlanView& p, void* ws, float* o, int ns_steps,
-                                hipStream_t s);
+// original orientation to o, or, with fuse, applies W <- fl(fl(W f) - fl(lr O))
+// to the parameter slices directly (O is then not stored).
+hipError_t launch_newton_schulz(const PlanView& p, void* ws, float* o, const FusedApply* fuse,
+                                int ns_steps, hipStream_t s);
 // W <- fl(fl(W*f) - fl(lr*O)) scattered into the slices.
 hipError_t launch_apply(const PlanView& p, void* params, int param_dtype, const float* o,
                         float decay, float lr, hipStream_t s);
