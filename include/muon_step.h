@@ -29,8 +29,15 @@
  * The Frobenius norm is a deterministic float32 reduction.  Newton-Schulz
  * runs either on bfloat16 MFMA with float32 accumulation and float32
  * epilogues, X/A/B stored as bfloat16 (MUON_GEMM_BF16_MFMA), or entirely in
- * float32 on the float32 MFMA (MUON_GEMM_F32).  O = fl(s * x) in float32.
- * Results are deterministic and do not depend on the order of descriptors.
+ * float32 on the float32 MFMA (MUON_GEMM_F32).  The first iterate is stored
+ * as U itself (rounded to the Newton-Schulz type) and the normalization is
+ * applied in float32 inside the first iteration: A0 = inv^2 (U U^T),
+ * X1 = inv (a U + B0 U), inv = 1 / (||U||_F + 1e-7) -- the same iterates as
+ * X0 = U / (||U||_F + 1e-7), with one rounding fewer.  With ns_steps == 0,
+ * O = fl(s * X0) with X0 rounded to the Newton-Schulz type.  O = fl(s * x)
+ * in float32.  Results are deterministic and do not depend on the order of
+ * descriptors; muon_step equals muon_apply(muon_orthogonalize(muon_momentum))
+ * bit for bit.
  *
  * Buffers.  All buffer pointers are device pointers allocated by the caller,
  * who keeps ownership.  Descriptor arrays are host memory read during the

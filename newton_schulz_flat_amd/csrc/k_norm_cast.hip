@@ -1,8 +1,18 @@
 // Frobenius normalization and layout change into the Newton-Schulz
 // orientation, on gfx950.
 //
-// norm_kernel: one workgroup per matrix sums that matrix's per-chunk partial
-// sums of squares in a fixed order and stores inv = 1 / (sqrt(sum) + 1e-7).
+// norm_kernel: one workgroup per matrix sums that matrix's partial sums of
+// squares (per elementwise chunk, or per 64 x 64 tile) in a fixed order and
+// stores inv = 1 / (sqrt(sum) + 1e-7).
+//
+// front_cast_kernel: one workgroup per 64 x 64 tile of the padded
+// NS-orientation matrix (the tiles of cast_kernel).  It reads the matching
+// block of G and M (or of U) along U's rows, computes M <- fl(fl(beta M) + G)
+// (stored) and U = fl(fl(beta M) + G) (or M) in float32 exactly as the
+// elementwise front kernel does, stores U rounded to the Newton-Schulz type --
+// not yet divided by its norm: the first iteration applies 1 / ||U|| in its
+// float32 epilogues -- in NS orientation, and writes the tile's sum of squares
+// of U (fixed order) for norm_kernel.  One pass replaces front + cast.
 //
 // cast_kernel: one workgroup per 64 x 64 tile of the padded NS-orientation
 // matrix X0 (rp x cp).  It reads the matching 64 x 64 block of U in U's own
@@ -24,10 +34,11 @@ constexpr int kNormThreads = 256;
 
 __global__ __launch_bounds__(kNormThreads) void norm_kernel(const MatInfo* __restrict__ mats,
                                                             const float* __restrict__ partial,
-                                                            float* __restrict__ inv) {
+                                                            float* __restrict__ inv, int per_tile) {
     __shared__ float red[kNormThreads];
     const int mi = blockIdx.x;
-    const int begin = mats[mi].chunk_begin, count = mats[mi].n_chunks;
+    const int begin = per_tile ? mats[mi].cast_begin : mats[mi].chunk_begin;
+    const int count = per_tile ? mats[mi].n_cast : mats[mi].n_chunks;
     float s = 0.f;
     for (int i = threadIdx.x; i < count; i += kNormThreads) s += partial[begin + i];
     red[threadIdx.x] = s;
@@ -103,12 +114,131 @@ __global__ __launch_bounds__(256) void cast_kernel(const MatInfo* __restrict__ m
     }
 }
 
+template <typename TX, bool kStep>
+__global__ __launch_bounds__(256) void front_cast_kernel(const MatInfo* __restrict__ mats,
+                                                         const int32_t* __restrict__ prefix, int n,
+                                                         const float* __restrict__ g, float* __restrict__ m,
+                                                         const float* __restrict__ u_in, float beta,
+                                                         int nesterov, TX* __restrict__ x,
+                                                         float* __restrict__ partial) {
+    constexpr int T = kCastTile;
+    __shared__ float tile[T][T + 1];
+    __shared__ float wsum[4];
+    const int blk = blockIdx.x;
+    const int mi = owner_of(prefix, n, blk);
+    const MatInfo& mt = mats[mi];
+    const int t = blk - mt.cast_begin;
+    const int ntj = mt.cp / T;
+    const int ti = t / ntj, tj = t % ntj;
+    const bool tall = mt.tall != 0;
+    // Tile origin in U's own (R x C) coordinates.
+    const int ur0 = tall ? tj * T : ti * T;
+    const int uc0 = tall ? ti * T : tj * T;
+    const bool vec = (mt.C & 3) == 0;  // rows start 16-byte aligned
+    float ss = 0.f;
+    // 64 rows x 16 four-element segments; 16 consecutive threads cover one row
+#pragma unroll
+    for (int it = 0; it < T * T / 4 / 256; ++it) {
+        const int seg = it * 256 + int(threadIdx.x);
+        const int rr = seg >> 4, c4 = (seg & 15) * 4;
+        const int gr = ur0 + rr, gc = uc0 + c4;
+        float uv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (gr < mt.R && gc < mt.C) {
+            const int64_t e = mt.off + int64_t(gr) * mt.C + gc;
+            if (vec && gc + 3 < mt.C) {
+                if (kStep) {
+                    const float4 gv = *reinterpret_cast<const float4*>(g + e);
+                    const float4 mv = *reinterpret_cast<const float4*>(m + e);
+                    const float g4[4] = {gv.x, gv.y, gv.z, gv.w};
+                    const float m4[4] = {mv.x, mv.y, mv.z, mv.w};
+                    float m1[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        m1[q] = beta * m4[q] + g4[q];
+                        uv[q] = nesterov ? beta * m1[q] + g4[q] : m1[q];
+                    }
+                    *reinterpret_cast<float4*>(m + e) = make_float4(m1[0], m1[1], m1[2], m1[3]);
+                } else {
+                    const float4 q4 = *reinterpret_cast<const float4*>(u_in + e);
+                    uv[0] = q4.x, uv[1] = q4.y, uv[2] = q4.z, uv[3] = q4.w;
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (gc + q < mt.C) {
+                        if (kStep) {
+                            const float m1 = beta * m[e + q] + g[e + q];
+                            m[e + q] = m1;
+                            uv[q] = nesterov ? beta * m1 + g[e + q] : m1;
+                        } else {
+                            uv[q] = u_in[e + q];
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            tile[rr][c4 + q] = uv[q];
+            ss = ss + uv[q] * uv[q];
+        }
+    }
+    // deterministic block sum: fixed shuffle tree, then the 4 wave sums in order
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    if (threadIdx.x == 0) partial[blk] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+    TX* xm = x + mt.x_off;
+    // X[i][j], i = ti*T + a, j = tj*T + b  (native element tile[a][b] or tile[b][a]);
+    // each thread writes 4 consecutive elements of a row
+    for (int idx = threadIdx.x; idx < T * T / 4; idx += 256) {
+        const int a = idx / (T / 4), b = (idx % (T / 4)) * 4;
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = tall ? tile[b + q][a] : tile[a][b + q];
+        store_x4(xm + int64_t(ti * T + a) * mt.cp + tj * T + b, v);
+    }
+}
+
 }  // namespace
 
-hipError_t launch_norm(const PlanView& p, const float* partial, float* inv, hipStream_t s) {
+hipError_t launch_norm(const PlanView& p, const float* partial, float* inv, bool per_tile,
+                       hipStream_t s) {
     if (p.n == 0) return hipSuccess;
     LaunchTimer timer("norm", s);
-    norm_kernel<<<dim3(unsigned(p.n)), dim3(kNormThreads), 0, s>>>(p.mats, partial, inv);
+    norm_kernel<<<dim3(unsigned(p.n)), dim3(kNormThreads), 0, s>>>(p.mats, partial, inv,
+                                                                   per_tile ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_front_cast(const PlanView& p, const float* grads, float* momentum,
+                             const float* u, float beta, int nesterov, void* ws, float* partial,
+                             hipStream_t s) {
+    if (p.total_cast == 0) return hipSuccess;
+    const bool step = u == nullptr;
+    LaunchTimer timer(step ? "front_cast" : "sumsq_cast", s);
+    unsigned char* w = static_cast<unsigned char*>(ws);
+    const dim3 grid{static_cast<unsigned>(p.total_cast)}, block{256};
+    if (p.gemm_mode == MUON_GEMM_F32) {
+        float* x = reinterpret_cast<float*>(w + p.ws.x[0]);
+        if (step)
+            front_cast_kernel<float, true><<<grid, block, 0, s>>>(p.mats, p.cast_prefix, p.n, grads,
+                                                                  momentum, nullptr, beta, nesterov,
+                                                                  x, partial);
+        else
+            front_cast_kernel<float, false><<<grid, block, 0, s>>>(p.mats, p.cast_prefix, p.n, nullptr,
+                                                                   nullptr, u, 0.f, 0, x, partial);
+    } else {
+        uint16_t* x = reinterpret_cast<uint16_t*>(w + p.ws.x[0]);
+        if (step)
+            front_cast_kernel<uint16_t, true><<<grid, block, 0, s>>>(p.mats, p.cast_prefix, p.n, grads,
+                                                                     momentum, nullptr, beta, nesterov,
+                                                                     x, partial);
+        else
+            front_cast_kernel<uint16_t, false><<<grid, block, 0, s>>>(p.mats, p.cast_prefix, p.n,
+                                                                      nullptr, nullptr, u, 0.f, 0, x,
+                                                                      partial);
+    }
     return hipGetLastError();
 }
 

@@ -56,6 +56,10 @@ struct NsArgs {
     float* o;       // O (last iteration), laid out like the gradients
     float ca, cb, cc;
     int last;
+    // Iteration 0 (first != 0) works on U itself: its products are scaled by
+    // the matrix's inv = 1 / ||U|| (A0 = inv^2 U U^T, X1 = inv (a U + B0 U)).
+    const float* inv;
+    int first;
     // fused apply on the last iteration (fuse != 0): W <- fl(fl(W decay) - fl(lr O))
     void* params;
     float decay, lr;
@@ -499,6 +503,10 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
     const int row0 = ti * TILE + wm * G::kWm + hk * 4;
     const int col0 = tj * TILE + wn * G::kWn + lr;
     const float ca = args.ca, cb = args.cb, cc = args.cc;
+    // iteration-0 normalization (exactly 1 afterwards)
+    const float inv0 = args.first ? args.inv[tile.mat] : 1.f;
+    const float sa = STAGE == kStageA ? inv0 * inv0 : 1.f;  // stage A: A0 = inv^2 U U^T
+    const float xs = inv0;                                  // stage X: X1 = inv (a U + B0 U)
     const TE* xc = static_cast<const TE*>(args.x_cur) + mt.x_off;
     // X (row layout) at fragment (i, j), group g
     auto x_row = [&](int i, int j, int g) {
@@ -571,7 +579,7 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
 #pragma unroll
                             for (int t = 0; t < 4; ++t)
                                 v[t] = STAGE == kStageB ? cb * ov4[t] + cc * acc[i][j][g * 4 + t]
-                                                        : ca * ov4[t] + acc[i][j][g * 4 + t];
+                                                        : xs * (ca * ov4[t] + acc[i][j][g * 4 + t]);
                             pk[i][j][g][0] = pack_bf16(v[0], v[1]);
                             pk[i][j][g][1] = pack_bf16(v[2], v[3]);
                         }
@@ -583,8 +591,8 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                     for (int j = 0; j < kNj; ++j)
 #pragma unroll
                         for (int g = 0; g < 4; ++g) {
-                            pk[i][j][g][0] = pack_bf16(acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1]);
-                            pk[i][j][g][1] = pack_bf16(acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]);
+                            pk[i][j][g][0] = pack_bf16(sa * acc[i][j][g * 4 + 0], sa * acc[i][j][g * 4 + 1]);
+                            pk[i][j][g][1] = pack_bf16(sa * acc[i][j][g * 4 + 2], sa * acc[i][j][g * 4 + 3]);
                         }
             }
             // column-major staging: staged row = output column j*32 + lr, 4 rows per lane
@@ -641,12 +649,12 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                         const int gj = col0 + j * 32;
                         float v[4], w[4], ov[4];
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) v[t] = acc[i][j][g * 4 + t];
+                        for (int t = 0; t < 4; ++t) v[t] = sa * acc[i][j][g * 4 + t];
                         if (STAGE == kStageX) {
                             quad_transpose(v, w, s4);
                             decode4(raw[j][g], ov);
 #pragma unroll
-                            for (int t = 0; t < 4; ++t) w[t] = ca * ov[t] + w[t];
+                            for (int t = 0; t < 4; ++t) w[t] = xs * (ca * ov[t] + w[t]);
                         } else {
                             if (STAGE == kStageB) {
                                 decode4(raw[j][g], ov);
@@ -698,7 +706,7 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                         float xcol[4];
                         quad_transpose(xv, xcol, s4);
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) v[t] = sc * (ca * xcol[t] + acc[i][j][g * 4 + t]);
+                        for (int t = 0; t < 4; ++t) v[t] = sc * (xs * (ca * xcol[t] + acc[i][j][g * 4 + t]));
                         *reinterpret_cast<float4*>(wl + (j * 32 + lr) * kPT + g * 8 + (lane >> 5) * 4) =
                             make_float4(v[0], v[1], v[2], v[3]);
                     } else {
@@ -707,7 +715,7 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                         for (int t = 0; t < 4; ++t) v[t] = acc[i][j][g * 4 + t];
                         quad_transpose(v, w, s4);
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) w[t] = sc * (ca * xv[t] + w[t]);
+                        for (int t = 0; t < 4; ++t) w[t] = sc * (xs * (ca * xv[t] + w[t]));
                         *reinterpret_cast<float4*>(wl + (g * 8 + (lane >> 5) * 4 + s4) * kPN + j * 32 + lr - s4) =
                             make_float4(w[0], w[1], w[2], w[3]);
                     }
@@ -800,6 +808,8 @@ hipError_t launch_newton_schulz(const PlanView& p, void* ws, float* o, const Fus
         a.cb = kNsB;
         a.cc = kNsC;
         a.last = it == ns_steps - 1;
+        a.first = it == 0;
+        a.inv = reinterpret_cast<const float*>(w + p.ws.inv);
         if (fuse && a.last) {
             a.params = fuse->params;
             a.decay = fuse->decay;

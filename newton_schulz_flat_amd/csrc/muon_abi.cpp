@@ -152,14 +152,20 @@ int muon_step(void* params, int param_dtype, int64_t n_param_elems, const float*
     volatile float lrwd = lr * weight_decay;
     const float decay = 1.0f - lrwd;
 
-    TRY_HIP(muon::launch_front(p, grads, momentum, u, partial, beta, nesterov, stream), "front");
-    TRY_HIP(muon::launch_norm(p, partial, inv, stream), "norm");
-    TRY_HIP(muon::launch_cast(p, u, inv, ws, ns_steps == 0 ? u : nullptr, stream), "cast");
     if (ns_steps > 0) {
-        // the last iteration applies the update itself (same roundings as the apply phase)
+        // momentum, input and first iterate in one pass; the norm is folded into
+        // iteration 0, and the last iteration applies the update itself (same
+        // roundings as the apply phase)
+        TRY_HIP(muon::launch_front_cast(p, grads, momentum, nullptr, beta, nesterov, ws, partial,
+                                        stream),
+                "front");
+        TRY_HIP(muon::launch_norm(p, partial, inv, true, stream), "norm");
         const muon::FusedApply fuse{params, param_dtype, decay, lr};
         TRY_HIP(muon::launch_newton_schulz(p, ws, u, &fuse, ns_steps, stream), "newton-schulz");
     } else {
+        TRY_HIP(muon::launch_front(p, grads, momentum, u, partial, beta, nesterov, stream), "front");
+        TRY_HIP(muon::launch_norm(p, partial, inv, false, stream), "norm");
+        TRY_HIP(muon::launch_cast(p, u, inv, ws, u, stream), "cast");
         TRY_HIP(muon::launch_apply(p, params, param_dtype, u, decay, lr, stream), "apply");
     }
     return MUON_OK;
@@ -213,11 +219,16 @@ int muon_orthogonalize(const float* u, float* o_out, int64_t n_elems,
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     float* partial = reinterpret_cast<float*>(ws + p.ws.partial);
     float* inv = reinterpret_cast<float*>(ws + p.ws.inv);
-    TRY_HIP(muon::launch_sumsq(p, u, partial, stream), "sum of squares");
-    TRY_HIP(muon::launch_norm(p, partial, inv, stream), "norm");
-    TRY_HIP(muon::launch_cast(p, u, inv, ws, ns_steps == 0 ? o_out : nullptr, stream), "cast");
-    if (ns_steps > 0)
+    if (ns_steps > 0) {
+        TRY_HIP(muon::launch_front_cast(p, nullptr, nullptr, u, 0.f, 0, ws, partial, stream),
+                "sum of squares and cast");
+        TRY_HIP(muon::launch_norm(p, partial, inv, true, stream), "norm");
         TRY_HIP(muon::launch_newton_schulz(p, ws, o_out, nullptr, ns_steps, stream), "newton-schulz");
+    } else {
+        TRY_HIP(muon::launch_sumsq(p, u, partial, stream), "sum of squares");
+        TRY_HIP(muon::launch_norm(p, partial, inv, false, stream), "norm");
+        TRY_HIP(muon::launch_cast(p, u, inv, ws, o_out, stream), "cast");
+    }
     return MUON_OK;
 }
 

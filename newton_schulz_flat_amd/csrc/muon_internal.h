@@ -169,8 +169,18 @@ hipError_t launch_front(const PlanView& p, const float* grads, float* momentum, 
                         float* partial, float beta, int nesterov, hipStream_t s);
 // Per-chunk sum of squares of an existing U.
 hipError_t launch_sumsq(const PlanView& p, const float* u, float* partial, hipStream_t s);
-// Per-matrix 1 / (sqrt(sum of partials) + eps).
-hipError_t launch_norm(const PlanView& p, const float* partial, float* inv, hipStream_t s);
+// Per-matrix 1 / (sqrt(sum of partials) + eps); partials per elementwise chunk,
+// or per 64 x 64 cast tile (per_tile).
+hipError_t launch_norm(const PlanView& p, const float* partial, float* inv, bool per_tile,
+                       hipStream_t s);
+// One pass per 64 x 64 tile: with u == nullptr, momentum and input from grads
+// and momentum (momentum updated); else U is read.  Writes U, rounded to the NS
+// type but not normalized, as the first iterate in NS orientation (zero
+// padding) and the per-tile sums of squares of U.  The Newton-Schulz iteration
+// 0 then applies 1 / ||U|| (launch_newton_schulz with the norm folded).
+hipError_t launch_front_cast(const PlanView& p, const float* grads, float* momentum,
+                             const float* u, float beta, int nesterov, void* ws, float* partial,
+                             hipStream_t s);
 // X0 = cast(U * inv) in NS orientation into the first X region, zero
 // padding; when o_direct is non-null (ns_steps == 0) write O = s * X0 there
 // instead.
@@ -183,9 +193,12 @@ struct FusedApply {
     int param_dtype;
     float decay, lr;
 };
-// ns_steps >= 1 Newton-Schulz iterations; the last writes O = s * X in the
-// original orientation to o, or, with fuse, applies W <- fl(fl(W f) - fl(lr O))
-// to the parameter slices directly (O is then not stored).
+// ns_steps >= 1 Newton-Schulz iterations on the first iterate that
+// launch_front_cast stored (U unnormalized; iteration 0 scales its products by
+// the per-matrix 1 / ||U||: A0 = inv^2 (U U^T), X1 = inv (a U + B0 U)); the last
+// writes O = s * X in the original orientation to o, or, with fuse, applies
+// W <- fl(fl(W f) - fl(lr O)) to the parameter slices directly (O is then not
+// stored).
 hipError_t launch_newton_schulz(const PlanView& p, void* ws, float* o, const FusedApply* fuse,
                                 int ns_steps, hipStream_t s);
 // W <- fl(fl(W*f) - fl(lr*O)) scattered into the slices.

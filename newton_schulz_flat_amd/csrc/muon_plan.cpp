@@ -105,8 +105,9 @@ Geometry build_geometry(const muon_matrix_desc_t* d, int64_t n, int gemm_mode) {
     at = align_up(at + size_t(g_elems) * es, kWsAlign);
     w.b = at;
     at = align_up(at + size_t(g_elems) * es, kWsAlign);
+    // partial sums: one per elementwise chunk or one per cast tile
     w.partial = at;
-    at = align_up(at + size_t(chunks) * 4, kWsAlign);
+    at = align_up(at + size_t(std::max<int64_t>(chunks, casts)) * 4, kWsAlign);
     w.inv = at;
     at = align_up(at + size_t(n) * 4, kWsAlign);
     w.total = std::max<size_t>(at, kWsAlign);
