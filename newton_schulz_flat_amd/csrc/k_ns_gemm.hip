@@ -386,36 +386,49 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
     // per lane; its instruction order is fixed with scheduling barriers so
     // that each MFMA is followed by at most a few memory instructions:
     //   q = 0, 1, 2: fragments of step q+1 are read from LDS (double-buffered
-    //                registers);
-    //   q = 2:       the next block, already in registers, is written to the
-    //                other LDS buffer, then all waves meet at the barrier;
+    //                registers); after step 2 all waves meet at the barrier,
+    //                after which this block's LDS buffer is free;
     //   q = 3:       the MFMAs run on fragments already in registers while the
-    //                fragments of step 0 of the next block are read and the
-    //                global loads of the block after it are issued.
-    // Keeping step 3's MFMAs behind the barrier gives the matrix pipe work while
-    // every wave refills its fragments.  Blocks past the end reload the last
-    // block (valid, unused copies) so the loop stays branch free.
+    //                fragments of step 0 of the next block are read, block
+    //                kb + 2 (in registers since step 3 of the previous block)
+    //                is written into the freed buffer, and the global loads of
+    //                block kb + 3 are issued.
+    // A global load thus has one whole K block to arrive before it is
+    // consumed, and step 3's MFMAs give the matrix pipe work while every wave
+    // refills its fragments.  Blocks past the end reload the last block
+    // (valid, unused copies) so the loop stays branch free.
     const int nkb = K / kBk;
     constexpr int kMfma = kMi * kNj;  // MFMAs per step q (per K sub-step for bf16)
     auto q_off = [&](int blk) -> int64_t {
         return (kTransQ || kQLdsT) ? int64_t(blk) * kBk * cp : int64_t(blk) * kBk;
     };
     u32x4 pa[kL], pb[kL];
-#pragma unroll
-    for (int l = 0; l < kL; ++l) {
-        pa[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep);
-        pb[l] = *reinterpret_cast<const u32x4*>(gq + l * qstep);
-    }
-#pragma unroll
-    for (int l = 0; l < kL; ++l) *reinterpret_cast<u32x4*>(lds + lds_st + l * kLdsPass) = pa[l];
-#pragma unroll
-    for (int w = 0; w < kQW; ++w) store_q<kTransQ, kL>(lds + q_st, pb, w, q_pass);
     {
-        const int b1 = nkb > 1 ? 1 : 0;
+        // blocks 0 and 1 into both LDS buffers, block 2 into the registers
+        u32x4 pa1[kL], pb1[kL];
+        const int b1 = nkb > 1 ? 1 : 0, b2 = nkb > 2 ? 2 : nkb - 1;
 #pragma unroll
         for (int l = 0; l < kL; ++l) {
-            pa[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep + int64_t(b1) * kBk);
-            pb[l] = *reinterpret_cast<const u32x4*>(gq + l * qstep + q_off(b1));
+            pa[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep);
+            pb[l] = *reinterpret_cast<const u32x4*>(gq + l * qstep);
+        }
+#pragma unroll
+        for (int l = 0; l < kL; ++l) {
+            pa1[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep + int64_t(b1) * kBk);
+            pb1[l] = *reinterpret_cast<const u32x4*>(gq + l * qstep + q_off(b1));
+        }
+#pragma unroll
+        for (int l = 0; l < kL; ++l) *reinterpret_cast<u32x4*>(lds + lds_st + l * kLdsPass) = pa[l];
+#pragma unroll
+        for (int w = 0; w < kQW; ++w) store_q<kTransQ, kL>(lds + q_st, pb, w, q_pass);
+#pragma unroll
+        for (int l = 0; l < kL; ++l) *reinterpret_cast<u32x4*>(lds + kBuf + lds_st + l * kLdsPass) = pa1[l];
+#pragma unroll
+        for (int w = 0; w < kQW; ++w) store_q<kTransQ, kL>(lds + kBuf + q_st, pb1, w, q_pass);
+#pragma unroll
+        for (int l = 0; l < kL; ++l) {
+            pa[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep + int64_t(b2) * kBk);
+            pb[l] = *reinterpret_cast<const u32x4*>(gq + l * qstep + q_off(b2));
         }
     }
     __syncthreads();
@@ -429,14 +442,13 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
         fb[0][j] = kQLdsT ? read_tr(lds + fbt_off + j * 64, 4 * kS)
                           : *reinterpret_cast<const u32x4*>(lds + fb_off + j * 32 * kLdsStride);
     for (int kb = 0; kb < nkb; ++kb) {
-        const int b2 = kb + 2 < nkb ? kb + 2 : nkb - 1;  // block loaded during step 3
-        const int64_t k2 = int64_t(b2) * kBk, qk2 = q_off(b2);
-        const unsigned char* buf = lds + (kb & 1) * kBuf;
-        unsigned char* nbuf = lds + ((kb + 1) & 1) * kBuf;
+        const int b3 = kb + 3 < nkb ? kb + 3 : nkb - 1;  // block loaded during step 3
+        const int64_t k3 = int64_t(b3) * kBk, qk3 = q_off(b3);
+        unsigned char* buf = lds + (kb & 1) * kBuf;
+        const unsigned char* nbuf = lds + ((kb + 1) & 1) * kBuf;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int cur = q & 1;
-            // fragments read during this step: step q+1 of this block, or step 0 of the next
             const unsigned char* rbuf = q < 3 ? buf : nbuf;
             const int rq = q < 3 ? q + 1 : 0;
 #pragma unroll
@@ -465,25 +477,32 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                         fb[cur ^ 1][rd - kMi] = *reinterpret_cast<const u32x4*>(
                             rbuf + fb_off + (rd - kMi) * 32 * kLdsStride + rq * 16);
                 }
-                if (q == 2) {
+                if (q == 3) {
+                    // this block's buffer is free: block kb + 2 goes in, then block kb + 3 is loaded
 #pragma unroll
                     for (int l = m; l < kL + kQW; l += kMfma) {
                         if (l < kL)
-                            *reinterpret_cast<u32x4*>(nbuf + lds_st + l * kLdsPass) = pa[l];
+                            *reinterpret_cast<u32x4*>(buf + lds_st + l * kLdsPass) = pa[l];
                         else
-                            store_q<kTransQ, kL>(nbuf + q_st, pb, l - kL, q_pass);
+                            store_q<kTransQ, kL>(buf + q_st, pb, l - kL, q_pass);
                     }
-                }
-                if (q == 3) {
+                    // a register is reloaded right after the write that consumed it;
+                    // the register-transposed Q writes read every pb, so those reloads
+                    // wait until all writes are issued (below)
 #pragma unroll
-                    for (int l = m; l < 2 * kL; l += kMfma) {
+                    for (int l = m; l < (kTransQ ? kL : 2 * kL); l += kMfma) {
                         if (l < kL)
-                            pa[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep + k2);
+                            pa[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep + k3);
                         else
-                            pb[l - kL] = *reinterpret_cast<const u32x4*>(gq + (l - kL) * qstep + qk2);
+                            pb[l - kL] = *reinterpret_cast<const u32x4*>(gq + (l - kL) * qstep + qk3);
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
+            }
+            if (kTransQ && q == 3) {
+#pragma unroll
+                for (int l = 0; l < kL; ++l)
+                    pb[l] = *reinterpret_cast<const u32x4*>(gq + l * qstep + qk3);
             }
             if (q == 2) __syncthreads();
         }
