@@ -85,7 +85,9 @@ extern "C" {
  *                 of rows*cols/n_shards elements; slice k of the update goes
  *                 to params[param_offset + k*shard_stride ...].  For
  *                 n_shards > 1 the slice length must be a multiple of 8.
- *   reserved      must be 0.
+ *   group         optimizer group of the matrix for muon_step_grouped
+ *                 (0 <= group < n_groups); must be 0 for every other entry
+ *                 point (muon_workspace_bytes accepts any group >= 0).
  * Every slice start must be 16-byte aligned within params.  Matrices must not
  * overlap each other in grads/momentum, nor slices each other in params. */
 typedef struct muon_matrix_desc {
@@ -95,7 +97,7 @@ typedef struct muon_matrix_desc {
     int64_t param_offset;
     int64_t shard_stride;
     int32_t n_shards;
-    int32_t reserved;
+    int32_t group;
 } muon_matrix_desc_t;
 
 typedef enum muon_status {
@@ -106,7 +108,7 @@ typedef enum muon_status {
     MUON_ERR_MISALIGNED = -4,          /* a matrix, slice or workspace start misaligned */
     MUON_ERR_OVERLAP = -5,             /* two descriptors' ranges intersect */
     MUON_ERR_ALIAS = -6,               /* two distinct buffers' address ranges intersect */
-    MUON_ERR_BAD_ARG = -7,             /* bad n, dtype, mode, ns_steps or non-finite scalar */
+    MUON_ERR_BAD_ARG = -7,             /* bad n, dtype, mode, ns_steps, group or non-finite scalar */
     MUON_ERR_WORKSPACE_TOO_SMALL = -8, /* workspace smaller than muon_workspace_bytes() */
     MUON_ERR_HIP = -9,                 /* a HIP runtime call failed (message has details) */
     MUON_ERR_INTERNAL = -10            /* should not happen; message has details */
@@ -156,6 +158,45 @@ int muon_momentum(const float* grads, float* momentum, float* u_out, int64_t n_s
 int muon_orthogonalize(const float* u, float* o_out, int64_t n_elems,
                        const muon_matrix_desc_t* descs, int64_t n, int ns_steps, int gemm_mode,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* One optimizer group of muon_step_grouped: the pages' optimizer keeps its
+ * settings per parameter group and maps every parameter to its group (page
+ * "core.distributed.fsdp.src.megatron_fsdp.experimental.muon", FsdpMuon._step_group,
+ * argument tensor_to_optimizer_group_index).  An array of groups lives in DEVICE
+ * memory and is read by the kernels when they run, so a captured graph
+ * replays with whatever values the array holds at replay time (the "optimizer
+ * CUDA graph" support listed on the page "fix(fsdp): drop stale MFSDP v2 guard
+ * rails ...", Megatron-Bridge PR #5933).  Values are not checked: NaN and
+ * infinities propagate; nesterov is true when non-zero. */
+typedef struct muon_group {
+    float lr;
+    float weight_decay;
+    float beta;
+    int32_t nesterov;
+} muon_group_t;
+
+/* The whole step with per-matrix optimizer groups and an optional bfloat16
+ * model copy.  Matrix i uses groups[descs[i].group]; its results equal, bit for
+ * bit, those of muon_step called with that group's scalars.
+ *   groups, n_groups  DEVICE array of n_groups (1..65536) muon_group_t, read
+ *                     during the kernels; must not overlap the other buffers.
+ *   model_copy        NULL, or -- with param_dtype MUON_DTYPE_F32 only -- a
+ *                     device bfloat16 buffer of n_param_elems elements, 16-byte
+ *                     aligned and laid out like params: every updated weight
+ *                     is also stored there, rounded to nearest even (float32
+ *                     master weights with a refreshed bfloat16 model copy: the
+ *                     pages' optimizer "refreshes its model weights itself",
+ *                     FsdpMuon class docstring and FsdpMuon.step; the
+ *                     precision-aware optimizer of PR #5933's page).
+ * Every other argument as muon_step.  Once the plan for a descriptor set
+ * exists (built by the first call with that set, which synchronizes the
+ * stream: make it outside graph capture), a call makes no allocation, memset
+ * or host synchronization and may be captured into a HIP graph. */
+int muon_step_grouped(void* params, int param_dtype, int64_t n_param_elems, void* model_copy,
+                      const float* grads, float* momentum, int64_t n_state_elems,
+                      const muon_matrix_desc_t* descs, int64_t n, const muon_group_t* groups,
+                      int32_t n_groups, int ns_steps, int gemm_mode, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
 
 /* Decay and update alone ("Opt step" step 6; FsdpMuon._apply_local_updates):
  * params slice k <- fl(fl(W*f) - fl(lr*O)), f = fl(1 - fl(lr*weight_decay)),

@@ -9,14 +9,17 @@ fallback.
 Entry points (same names as the C ABI):
 
 ``muon_step``           momentum, Nesterov input, Newton-Schulz, decay + apply
+``muon_step_grouped``   the same with per-matrix optimizer groups read from a
+                        device table (graph-capturable) and an optional
+                        bfloat16 copy of float32 weights
 ``muon_momentum``       momentum update and orthogonalization input only
 ``muon_orthogonalize``  Newton-Schulz orthogonalization (with shape scale) only
 ``muon_apply``          decoupled decay and update, scattered into slices
 ``muon_workspace_bytes``
 
 Descriptors are objects with ``offset, rows, cols`` and optionally
-``param_offset`` (default ``offset``), ``shard_stride`` (0) and ``n_shards``
-(1), or tuples in that field order.
+``param_offset`` (default ``offset``), ``shard_stride`` (0), ``n_shards`` (1)
+and ``group`` (0), or tuples in that field order.
 """
 
 from __future__ import annotations
@@ -36,9 +39,9 @@ MUON_GEMM_F32 = 1
 _MODES = {"bf16": MUON_GEMM_BF16_MFMA, "f32": MUON_GEMM_F32}
 
 #: C names of every exported entry point (mirrors include/muon_step.h).
-EXPORTS = ("muon_workspace_bytes", "muon_step", "muon_momentum", "muon_orthogonalize",
-           "muon_apply", "muon_profile_begin", "muon_profile_end", "muon_status_string",
-           "muon_last_error")
+EXPORTS = ("muon_workspace_bytes", "muon_step", "muon_step_grouped", "muon_momentum",
+           "muon_orthogonalize", "muon_apply", "muon_profile_begin", "muon_profile_end",
+           "muon_status_string", "muon_last_error")
 
 
 class MatrixDescC(ctypes.Structure):
@@ -46,7 +49,7 @@ class MatrixDescC(ctypes.Structure):
 
     _fields_ = [("offset", ctypes.c_int64), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
                 ("param_offset", ctypes.c_int64), ("shard_stride", ctypes.c_int64),
-                ("n_shards", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("n_shards", ctypes.c_int32), ("group", ctypes.c_int32)]
 
 
 class KernelTimeC(ctypes.Structure):
@@ -83,6 +86,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.muon_workspace_bytes.argtypes = [dp, i64, i32, ctypes.POINTER(sz)]
     lib.muon_step.argtypes = [p, i32, i64, p, p, i64, dp, i64, f32, f32, f32, i32, i32, i32, p,
                               sz, p]
+    lib.muon_step_grouped.argtypes = [p, i32, i64, p, p, p, i64, dp, i64, p, ctypes.c_int32, i32,
+                                      i32, p, sz, p]
     lib.muon_momentum.argtypes = [p, p, p, i64, dp, i64, f32, i32, p]
     lib.muon_orthogonalize.argtypes = [p, p, i64, dp, i64, i32, i32, p, sz, p]
     lib.muon_apply.argtypes = [p, i32, i64, p, i64, dp, i64, f32, f32, p]
@@ -92,8 +97,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.muon_status_string.restype = ctypes.c_char_p
     lib.muon_last_error.argtypes = []
     lib.muon_last_error.restype = ctypes.c_char_p
-    for name in ("muon_workspace_bytes", "muon_step", "muon_momentum", "muon_orthogonalize",
-                 "muon_apply", "muon_profile_begin", "muon_profile_end"):
+    for name in ("muon_workspace_bytes", "muon_step", "muon_step_grouped", "muon_momentum",
+                 "muon_orthogonalize", "muon_apply", "muon_profile_begin", "muon_profile_end"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -113,15 +118,17 @@ def descs_array(descs: Iterable) -> ctypes.Array:
     arr = (MatrixDescC * max(1, len(items)))()
     for k, d in enumerate(items):
         if isinstance(d, (tuple, list)):
-            vals = list(d) + [None] * (6 - len(d))
-            off, rows, cols, poff, stride, shards = vals[:6]
+            vals = list(d) + [None] * (7 - len(d))
+            off, rows, cols, poff, stride, shards, group = vals[:7]
         else:
             off, rows, cols = d.offset, d.rows, d.cols
             poff = getattr(d, "param_offset", None)
             stride = getattr(d, "shard_stride", None)
             shards = getattr(d, "n_shards", None)
+            group = getattr(d, "group", None)
         arr[k] = MatrixDescC(int(off), int(rows), int(cols), int(off if poff is None else poff),
-                             int(stride or 0), int(1 if shards is None else shards), 0)
+                             int(stride or 0), int(1 if shards is None else shards),
+                             int(group or 0))
     return arr
 
 
@@ -192,6 +199,49 @@ def muon_step(params, grads, momentum, descs, lr: float, weight_decay: float, be
                         lr, weight_decay, beta, int(bool(nesterov)), int(ns_steps), _mode(mode),
                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                         _stream(grads)))
+
+
+def group_table(groups, device):
+    """A device table of optimizer groups for ``muon_step_grouped``: rows of
+    ``(lr, weight_decay, beta, nesterov)``, stored as ``muon_group_t`` (three
+    float32 and one int32) in an int32 tensor of shape (len(groups), 4)."""
+    import numpy as np
+    import torch
+    rows = np.zeros((len(groups), 4), dtype=np.int32)
+    for k, (lr, wd, beta, nesterov) in enumerate(groups):
+        rows[k, :3] = np.array([lr, wd, beta], dtype=np.float32).view(np.int32)
+        rows[k, 3] = int(bool(nesterov))
+    return torch.from_numpy(rows).to(device)
+
+
+def muon_step_grouped(params, grads, momentum, descs, groups, ns_steps: int = 5,
+                      mode: str = "bf16", model_copy=None, workspace=None):
+    """One Muon step with per-matrix optimizer groups: descriptor ``group`` k
+    uses row k of ``groups`` (a ``group_table`` on the GPU, read when the
+    kernels run).  ``model_copy`` (bf16, shaped like float32 ``params``)
+    receives the updated weights rounded to bfloat16."""
+    import torch
+    _require(params, "params", (torch.float32, torch.bfloat16))
+    _require(grads, "grads", (torch.float32,))
+    _require(momentum, "momentum", (torch.float32,))
+    _require(groups, "groups", (torch.int32,))
+    if groups.dim() != 2 or groups.shape[1] != 4:
+        raise ValueError("groups must be a group_table of shape (n_groups, 4)")
+    copy_ptr = None
+    if model_copy is not None:
+        _require(model_copy, "model_copy", (torch.bfloat16,))
+        if model_copy.numel() != params.numel():
+            raise ValueError("model_copy must have as many elements as params")
+        copy_ptr = model_copy.data_ptr()
+    if workspace is None:
+        workspace = workspace_for(descs, mode, grads.device)
+    lib = load_library()
+    dt = MUON_DTYPE_BF16 if params.dtype == torch.bfloat16 else MUON_DTYPE_F32
+    check(lib.muon_step_grouped(params.data_ptr(), dt, params.numel(), copy_ptr, grads.data_ptr(),
+                                momentum.data_ptr(), grads.numel(), descs_array(descs),
+                                _count(descs), groups.data_ptr(), groups.shape[0], int(ns_steps),
+                                _mode(mode), workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), _stream(grads)))
 
 
 def muon_momentum(grads, momentum, u_out, descs, beta: float, nesterov: bool = True):

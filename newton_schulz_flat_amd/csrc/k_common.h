@@ -33,4 +33,25 @@ __device__ __forceinline__ uint16_t bf16_rne(float x) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
+// One matrix's optimizer scalars; decay = fl(1 - fl(lr * wd)), the same two
+// roundings as on the host.
+struct HyperVals {
+    float lr, decay, beta;
+    int nesterov;
+};
+__device__ __forceinline__ HyperVals hyper_for(const Hyper& h, const MatInfo& mt) {
+#pragma clang fp contract(off)
+    HyperVals v;
+    float wd;
+    if (h.groups != nullptr) {
+        const muon_group_t g = h.groups[mt.group];
+        v.lr = g.lr, wd = g.weight_decay, v.beta = g.beta, v.nesterov = g.nesterov != 0;
+    } else {
+        v.lr = h.lr, wd = h.weight_decay, v.beta = h.beta, v.nesterov = h.nesterov;
+    }
+    const float lrwd = v.lr * wd;
+    v.decay = 1.0f - lrwd;
+    return v;
+}
+
 }  // namespace muon

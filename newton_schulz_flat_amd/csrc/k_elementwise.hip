@@ -37,10 +37,13 @@ template <int kMode>
 __global__ __launch_bounds__(kEwThreads) void front_kernel(
     const MatInfo* __restrict__ mats, const int32_t* __restrict__ prefix, int n,
     const float* __restrict__ g, float* __restrict__ m, float* __restrict__ u,
-    float* __restrict__ partial, float beta, int nesterov) {
+    float* __restrict__ partial, Hyper h) {
     __shared__ float lds4[4];
     const int blk = blockIdx.x;
     const int mi = owner_of(prefix, n, blk);
+    const HyperVals hv = hyper_for(h, mats[mi]);
+    const float beta = hv.beta;
+    const int nesterov = hv.nesterov;
     const int64_t off = mats[mi].off;
     const int64_t end = off + mats[mi].numel;
     const int64_t base = off + int64_t(blk - mats[mi].chunk_begin) * kEwChunk;
@@ -121,10 +124,12 @@ __device__ __forceinline__ void store_w1(uint16_t* p, float v) { *p = bf16_rne(v
 template <typename TW>
 __global__ __launch_bounds__(kEwThreads) void apply_kernel(
     const MatInfo* __restrict__ mats, const int32_t* __restrict__ prefix, int n,
-    TW* __restrict__ w, const float* __restrict__ o, float decay, float lr) {
+    TW* __restrict__ w, const float* __restrict__ o, Hyper h, uint16_t* __restrict__ copy) {
     const int blk = blockIdx.x;
     const int mi = owner_of(prefix, n, blk);
     const MatInfo& mt = mats[mi];
+    const HyperVals hv = hyper_for(h, mt);
+    const float decay = hv.decay, lr = hv.lr;
     const int64_t numel = mt.numel, off = mt.off, poff = mt.poff;
     const int64_t slice = mt.slice_len, stride = mt.pstride;
     const bool sharded = slice != numel;
@@ -147,13 +152,16 @@ __global__ __launch_bounds__(kEwThreads) void apply_kernel(
             r.z = wv.z * decay - lr * ov.z;
             r.w = wv.w * decay - lr * ov.w;
             store_w(w + dst, r);
+            if (copy != nullptr) store_w(copy + dst, r);
         } else {
             for (int64_t k = j; k < numel && k < j + kEwVec; ++k) {
                 const int64_t s = sharded ? k / slice : 0;
                 const int64_t dst = poff + s * stride + (k - s * slice);
                 const float w1 = load_w1(w + dst) * decay;
                 const float t = lr * o[off + k];
-                store_w1(w + dst, w1 - t);
+                const float wn = w1 - t;
+                store_w1(w + dst, wn);
+                if (copy != nullptr) store_w1(copy + dst, wn);
             }
         }
     }
@@ -162,11 +170,11 @@ __global__ __launch_bounds__(kEwThreads) void apply_kernel(
 }  // namespace
 
 hipError_t launch_front(const PlanView& p, const float* grads, float* momentum, float* u,
-                        float* partial, float beta, int nesterov, hipStream_t s) {
+                        float* partial, const Hyper& h, hipStream_t s) {
     if (p.total_chunks == 0) return hipSuccess;
     LaunchTimer timer("front", s);
     front_kernel<0><<<dim3(unsigned(p.total_chunks)), dim3(kEwThreads), 0, s>>>(
-        p.mats, p.chunk_prefix, p.n, grads, momentum, u, partial, beta, nesterov);
+        p.mats, p.chunk_prefix, p.n, grads, momentum, u, partial, h);
     return hipGetLastError();
 }
 
@@ -174,21 +182,21 @@ hipError_t launch_sumsq(const PlanView& p, const float* u, float* partial, hipSt
     if (p.total_chunks == 0) return hipSuccess;
     LaunchTimer timer("sumsq", s);
     front_kernel<1><<<dim3(unsigned(p.total_chunks)), dim3(kEwThreads), 0, s>>>(
-        p.mats, p.chunk_prefix, p.n, nullptr, nullptr, const_cast<float*>(u), partial, 0.f, 0);
+        p.mats, p.chunk_prefix, p.n, nullptr, nullptr, const_cast<float*>(u), partial, Hyper{});
     return hipGetLastError();
 }
 
 hipError_t launch_apply(const PlanView& p, void* params, int param_dtype, const float* o,
-                        float decay, float lr, hipStream_t s) {
+                        const Hyper& h, uint16_t* model_copy, hipStream_t s) {
     if (p.total_chunks == 0) return hipSuccess;
     LaunchTimer timer("apply", s);
     const dim3 grid{static_cast<unsigned>(p.total_chunks)}, block{kEwThreads};
     if (param_dtype == MUON_DTYPE_BF16)
         apply_kernel<uint16_t><<<grid, block, 0, s>>>(p.mats, p.chunk_prefix, p.n,
-                                                      static_cast<uint16_t*>(params), o, decay, lr);
+                                                      static_cast<uint16_t*>(params), o, h, nullptr);
     else
         apply_kernel<float><<<grid, block, 0, s>>>(p.mats, p.chunk_prefix, p.n,
-                                                   static_cast<float*>(params), o, decay, lr);
+                                                   static_cast<float*>(params), o, h, model_copy);
     return hipGetLastError();
 }
 

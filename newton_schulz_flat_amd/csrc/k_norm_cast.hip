@@ -118,8 +118,8 @@ template <typename TX, bool kStep>
 __global__ __launch_bounds__(256) void front_cast_kernel(const MatInfo* __restrict__ mats,
                                                          const int32_t* __restrict__ prefix, int n,
                                                          const float* __restrict__ g, float* __restrict__ m,
-                                                         const float* __restrict__ u_in, float beta,
-                                                         int nesterov, TX* __restrict__ x,
+                                                         const float* __restrict__ u_in, Hyper h,
+                                                         TX* __restrict__ x,
                                                          float* __restrict__ partial) {
     constexpr int T = kCastTile;
     __shared__ float tile[T][T + 1];
@@ -135,6 +135,9 @@ __global__ __launch_bounds__(256) void front_cast_kernel(const MatInfo* __restri
     const int ur0 = tall ? tj * T : ti * T;
     const int uc0 = tall ? ti * T : tj * T;
     const bool vec = (mt.C & 3) == 0;  // rows start 16-byte aligned
+    const HyperVals hv = hyper_for(h, mt);
+    const float beta = hv.beta;
+    const int nesterov = hv.nesterov;
     float ss = 0.f;
     // 64 rows x 16 four-element segments; 16 consecutive threads cover one row
 #pragma unroll
@@ -212,7 +215,7 @@ hipError_t launch_norm(const PlanView& p, const float* partial, float* inv, bool
 }
 
 hipError_t launch_front_cast(const PlanView& p, const float* grads, float* momentum,
-                             const float* u, float beta, int nesterov, void* ws, float* partial,
+                             const float* u, const Hyper& h, void* ws, float* partial,
                              hipStream_t s) {
     if (p.total_cast == 0) return hipSuccess;
     const bool step = u == nullptr;
@@ -223,20 +226,18 @@ hipError_t launch_front_cast(const PlanView& p, const float* grads, float* momen
         float* x = reinterpret_cast<float*>(w + p.ws.x[0]);
         if (step)
             front_cast_kernel<float, true><<<grid, block, 0, s>>>(p.mats, p.cast_prefix, p.n, grads,
-                                                                  momentum, nullptr, beta, nesterov,
-                                                                  x, partial);
+                                                                  momentum, nullptr, h, x, partial);
         else
             front_cast_kernel<float, false><<<grid, block, 0, s>>>(p.mats, p.cast_prefix, p.n, nullptr,
-                                                                   nullptr, u, 0.f, 0, x, partial);
+                                                                   nullptr, u, Hyper{}, x, partial);
     } else {
         uint16_t* x = reinterpret_cast<uint16_t*>(w + p.ws.x[0]);
         if (step)
             front_cast_kernel<uint16_t, true><<<grid, block, 0, s>>>(p.mats, p.cast_prefix, p.n, grads,
-                                                                     momentum, nullptr, beta, nesterov,
-                                                                     x, partial);
+                                                                     momentum, nullptr, h, x, partial);
         else
             front_cast_kernel<uint16_t, false><<<grid, block, 0, s>>>(p.mats, p.cast_prefix, p.n,
-                                                                      nullptr, nullptr, u, 0.f, 0, x,
+                                                                      nullptr, nullptr, u, Hyper{}, x,
                                                                       partial);
     }
     return hipGetLastError();

@@ -60,9 +60,12 @@ struct NsArgs {
     // the matrix's inv = 1 / ||U|| (A0 = inv^2 U U^T, X1 = inv (a U + B0 U)).
     const float* inv;
     int first;
-    // fused apply on the last iteration (fuse != 0): W <- fl(fl(W decay) - fl(lr O))
+    // fused apply on the last iteration (fuse != 0): W <- fl(fl(W decay) - fl(lr O)),
+    // decay and lr of the matrix's optimizer group; model_copy: bfloat16 copy of
+    // float32 weights (or null)
     void* params;
-    float decay, lr;
+    Hyper hyper;
+    uint16_t* model_copy;
     int fuse, param_bf16;
 };
 
@@ -204,8 +207,8 @@ __device__ __forceinline__ void store_w1(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_w1(uint16_t* p, float v) { *p = bf16_rne(v); }
 
 template <typename TW>
-__device__ __forceinline__ void apply_span(TW* __restrict__ params, const MatInfo& mt, int64_t e,
-                                           int cnt, const float o[4], float decay, float lr) {
+__device__ __forceinline__ void apply_span(TW* __restrict__ params, uint16_t* copy, const MatInfo& mt,
+                                           int64_t e, int cnt, const float o[4], float decay, float lr) {
 #pragma clang fp contract(off)
     const int64_t slice = mt.slice_len;
     const bool sharded = slice != mt.numel;
@@ -225,6 +228,7 @@ __device__ __forceinline__ void apply_span(TW* __restrict__ params, const MatInf
             r[t] = w1 - u;
         }
         store_w4(params + dst, r);
+        if (copy != nullptr) store_w4(copy + dst, r);
     } else {
         // static indexing only: o[] must stay in registers
 #pragma unroll
@@ -232,10 +236,12 @@ __device__ __forceinline__ void apply_span(TW* __restrict__ params, const MatInf
             if (t < cnt) {
                 const int64_t j = e + t;
                 const int64_t k = sharded ? j / slice : 0;
-                TW* dst = params + mt.poff + k * mt.pstride + (j - k * slice);
-                const float w1 = load_w1(dst) * decay;
+                const int64_t at = mt.poff + k * mt.pstride + (j - k * slice);
+                const float w1 = load_w1(params + at) * decay;
                 const float u = lr * o[t];
-                store_w1(dst, w1 - u);
+                const float wn = w1 - u;
+                store_w1(params + at, wn);
+                if (copy != nullptr) store_w1(copy + at, wn);
             }
         }
     }
@@ -698,6 +704,7 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
         const int r = mt.r, c = mt.c;
         const bool tall = mt.tall != 0;
         const int rows_o = tall ? c : r, cols_o = tall ? r : c;  // O's shape
+        const HyperVals hv = hyper_for(args.hyper, mt);
         constexpr int kWn = G::kWn;
         constexpr int kPN = kWn + 4;  // float pitch, wide: 32 O rows of kWn
         constexpr int kPT = 32 + 4;   // float pitch, tall: kWn O rows of 32
@@ -756,9 +763,11 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                     const int64_t e = int64_t(a) * cols_o + b;
                     if (args.fuse) {
                         if (args.param_bf16)
-                            apply_span(static_cast<uint16_t*>(args.params), mt, e, cnt, ov, args.decay, args.lr);
+                            apply_span(static_cast<uint16_t*>(args.params), nullptr, mt, e, cnt, ov, hv.decay,
+                                       hv.lr);
                         else
-                            apply_span(static_cast<float*>(args.params), mt, e, cnt, ov, args.decay, args.lr);
+                            apply_span(static_cast<float*>(args.params), args.model_copy, mt, e, cnt, ov,
+                                       hv.decay, hv.lr);
                     } else if (cnt == 4 && (e & 3) == 0) {
                         store4(om + e, ov);
                     } else {
@@ -831,8 +840,8 @@ hipError_t launch_newton_schulz(const PlanView& p, void* ws, float* o, const Fus
         a.inv = reinterpret_cast<const float*>(w + p.ws.inv);
         if (fuse && a.last) {
             a.params = fuse->params;
-            a.decay = fuse->decay;
-            a.lr = fuse->lr;
+            a.hyper = fuse->hyper;
+            a.model_copy = fuse->model_copy;
             a.fuse = 1;
             a.param_bf16 = fuse->param_dtype == MUON_DTYPE_BF16;
         }

@@ -2,6 +2,7 @@
 // contracts, in include/muon_step.h).  Each entry point validates everything
 // on the host first, then fetches the cached plan and enqueues its kernels on
 // the caller's stream.  Nothing is thrown across the ABI.
+#include <climits>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -98,6 +99,73 @@ int check_workspace(const void* ws, size_t have, size_t need, Status* st) {
         if (e_ != hipSuccess) return finish((hip_fail(&st, e_, what), st)); \
     } while (0)
 
+// The whole step for muon_step and muon_step_grouped: validation of everything
+// but the scalars, then the launches.  h holds the scalars or the device group
+// array (n_groups groups).
+int run_step(Status& st, void* params, int param_dtype, int64_t n_param_elems, void* model_copy,
+             const float* grads, float* momentum, int64_t n_state_elems,
+             const muon_matrix_desc_t* descs, int64_t n, const muon::Hyper& h, int32_t n_groups,
+             int ns_steps, int gemm_mode, void* workspace, size_t workspace_bytes,
+             hipStream_t stream) {
+    TRY(muon::check_desc_shapes(descs, n, &st, n_groups));
+    TRY(check_mode(gemm_mode, &st));
+    TRY(check_ns_steps(ns_steps, &st));
+    if (param_dtype != MUON_DTYPE_F32 && param_dtype != MUON_DTYPE_BF16)
+        TRY(muon::check_param_ranges(descs, 0, 0, param_dtype, &st));
+    if (model_copy != nullptr && param_dtype != MUON_DTYPE_F32) {
+        st.code = MUON_ERR_BAD_ARG;
+        snprintf(st.msg, sizeof(st.msg), "model_copy needs float32 params (param_dtype %d)",
+                 param_dtype);
+        return finish(st);
+    }
+    if (n == 0) return MUON_OK;
+    TRY(check_null(params, "params", &st));
+    TRY(check_null(grads, "grads", &st));
+    TRY(check_null(momentum, "momentum", &st));
+    TRY(muon::check_state_ranges(descs, n, n_state_elems, "grads/momentum", &st));
+    TRY(muon::check_param_ranges(descs, n, n_param_elems, param_dtype, &st));
+    if (model_copy != nullptr && reinterpret_cast<uintptr_t>(model_copy) % 16 != 0) {
+        st.code = MUON_ERR_MISALIGNED;
+        snprintf(st.msg, sizeof(st.msg), "model_copy is not 16-byte aligned");
+        return finish(st);
+    }
+    const size_t need = muon::workspace_bytes_for(descs, n, gemm_mode);
+    TRY(check_workspace(workspace, workspace_bytes, need, &st));
+    const muon::Range ranges[6] = {
+        {params, param_bytes(param_dtype, n_param_elems), "params"},
+        {grads, size_t(n_state_elems) * 4, "grads"},
+        {momentum, size_t(n_state_elems) * 4, "momentum"},
+        {workspace, workspace_bytes, "workspace"},
+        {h.groups, h.groups ? size_t(n_groups) * sizeof(muon_group_t) : 0, "groups"},
+        {model_copy, model_copy ? size_t(n_param_elems) * 2 : 0, "model_copy"}};
+    TRY(muon::check_no_alias(ranges, 6, &st));
+
+    std::shared_ptr<const muon::PlanStore> plan;
+    TRY(muon::get_plan(descs, n, gemm_mode, stream, &plan, &st));
+    const muon::PlanView& p = muon::view_of(*plan);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    float* u = reinterpret_cast<float*>(ws + p.ws.u);
+    float* partial = reinterpret_cast<float*>(ws + p.ws.partial);
+    float* inv = reinterpret_cast<float*>(ws + p.ws.inv);
+    uint16_t* copy = static_cast<uint16_t*>(model_copy);
+    if (ns_steps > 0) {
+        // momentum, input and first iterate in one pass; the norm is folded into
+        // iteration 0, and the last iteration applies the update itself (same
+        // roundings as the apply phase)
+        TRY_HIP(muon::launch_front_cast(p, grads, momentum, nullptr, h, ws, partial, stream),
+                "front");
+        TRY_HIP(muon::launch_norm(p, partial, inv, true, stream), "norm");
+        const muon::FusedApply fuse{params, param_dtype, h, copy};
+        TRY_HIP(muon::launch_newton_schulz(p, ws, u, &fuse, ns_steps, stream), "newton-schulz");
+    } else {
+        TRY_HIP(muon::launch_front(p, grads, momentum, u, partial, h, stream), "front");
+        TRY_HIP(muon::launch_norm(p, partial, inv, false, stream), "norm");
+        TRY_HIP(muon::launch_cast(p, u, inv, ws, u, stream), "cast");
+        TRY_HIP(muon::launch_apply(p, params, param_dtype, u, h, copy, stream), "apply");
+    }
+    return MUON_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -107,7 +175,8 @@ int muon_workspace_bytes(const muon_matrix_desc_t* descs, int64_t n, int gemm_mo
     Status st{MUON_OK, ""};
     TRY(check_null(out_bytes, "out_bytes", &st));
     TRY(check_mode(gemm_mode, &st));
-    TRY(muon::check_desc_shapes(descs, n, &st));
+    // any group index is fine here: the workspace does not depend on groups
+    TRY(muon::check_desc_shapes(descs, n, &st, INT32_MAX));
     *out_bytes = muon::workspace_bytes_for(descs, n, gemm_mode);
     return MUON_OK;
 }
@@ -117,58 +186,32 @@ int muon_step(void* params, int param_dtype, int64_t n_param_elems, const float*
               float lr, float weight_decay, float beta, int nesterov, int ns_steps, int gemm_mode,
               void* workspace, size_t workspace_bytes, hipStream_t stream) {
     Status st{MUON_OK, ""};
-    TRY(muon::check_desc_shapes(descs, n, &st));
-    TRY(check_mode(gemm_mode, &st));
-    TRY(check_ns_steps(ns_steps, &st));
     TRY(check_flag(nesterov, "nesterov", &st));
     TRY(muon::check_scalar(lr, "lr", &st));
     TRY(muon::check_scalar(weight_decay, "weight_decay", &st));
     TRY(muon::check_scalar(beta, "beta", &st));
-    if (param_dtype != MUON_DTYPE_F32 && param_dtype != MUON_DTYPE_BF16)
-        TRY(muon::check_param_ranges(descs, 0, 0, param_dtype, &st));
-    if (n == 0) return MUON_OK;
-    TRY(check_null(params, "params", &st));
-    TRY(check_null(grads, "grads", &st));
-    TRY(check_null(momentum, "momentum", &st));
-    TRY(muon::check_state_ranges(descs, n, n_state_elems, "grads/momentum", &st));
-    TRY(muon::check_param_ranges(descs, n, n_param_elems, param_dtype, &st));
-    const size_t need = muon::workspace_bytes_for(descs, n, gemm_mode);
-    TRY(check_workspace(workspace, workspace_bytes, need, &st));
-    const muon::Range ranges[4] = {
-        {params, param_bytes(param_dtype, n_param_elems), "params"},
-        {grads, size_t(n_state_elems) * 4, "grads"},
-        {momentum, size_t(n_state_elems) * 4, "momentum"},
-        {workspace, workspace_bytes, "workspace"}};
-    TRY(muon::check_no_alias(ranges, 4, &st));
+    const muon::Hyper h{nullptr, lr, weight_decay, beta, nesterov};
+    return run_step(st, params, param_dtype, n_param_elems, nullptr, grads, momentum, n_state_elems,
+                    descs, n, h, 1, ns_steps, gemm_mode, workspace, workspace_bytes, stream);
+}
 
-    std::shared_ptr<const muon::PlanStore> plan;
-    TRY(muon::get_plan(descs, n, gemm_mode, stream, &plan, &st));
-    const muon::PlanView& p = muon::view_of(*plan);
-    unsigned char* ws = static_cast<unsigned char*>(workspace);
-    float* u = reinterpret_cast<float*>(ws + p.ws.u);
-    float* partial = reinterpret_cast<float*>(ws + p.ws.partial);
-    float* inv = reinterpret_cast<float*>(ws + p.ws.inv);
-    // decay factor f = fl(1 - fl(lr * wd)), float32 on the host
-    volatile float lrwd = lr * weight_decay;
-    const float decay = 1.0f - lrwd;
-
-    if (ns_steps > 0) {
-        // momentum, input and first iterate in one pass; the norm is folded into
-        // iteration 0, and the last iteration applies the update itself (same
-        // roundings as the apply phase)
-        TRY_HIP(muon::launch_front_cast(p, grads, momentum, nullptr, beta, nesterov, ws, partial,
-                                        stream),
-                "front");
-        TRY_HIP(muon::launch_norm(p, partial, inv, true, stream), "norm");
-        const muon::FusedApply fuse{params, param_dtype, decay, lr};
-        TRY_HIP(muon::launch_newton_schulz(p, ws, u, &fuse, ns_steps, stream), "newton-schulz");
-    } else {
-        TRY_HIP(muon::launch_front(p, grads, momentum, u, partial, beta, nesterov, stream), "front");
-        TRY_HIP(muon::launch_norm(p, partial, inv, false, stream), "norm");
-        TRY_HIP(muon::launch_cast(p, u, inv, ws, u, stream), "cast");
-        TRY_HIP(muon::launch_apply(p, params, param_dtype, u, decay, lr, stream), "apply");
+int muon_step_grouped(void* params, int param_dtype, int64_t n_param_elems, void* model_copy,
+                      const float* grads, float* momentum, int64_t n_state_elems,
+                      const muon_matrix_desc_t* descs, int64_t n, const muon_group_t* groups,
+                      int32_t n_groups, int ns_steps, int gemm_mode, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+    Status st{MUON_OK, ""};
+    if (n_groups < 1 || n_groups > muon::kMaxGroups) {
+        st.code = MUON_ERR_BAD_ARG;
+        snprintf(st.msg, sizeof(st.msg), "n_groups = %d is outside [1, %d]", n_groups,
+                 muon::kMaxGroups);
+        return finish(st);
     }
-    return MUON_OK;
+    if (n > 0) TRY(check_null(groups, "groups", &st));
+    const muon::Hyper h{groups, 0.f, 0.f, 0.f, 0};
+    return run_step(st, params, param_dtype, n_param_elems, model_copy, grads, momentum,
+                    n_state_elems, descs, n, h, n_groups, ns_steps, gemm_mode, workspace,
+                    workspace_bytes, stream);
 }
 
 int muon_momentum(const float* grads, float* momentum, float* u_out, int64_t n_state_elems,
@@ -190,8 +233,8 @@ int muon_momentum(const float* grads, float* momentum, float* u_out, int64_t n_s
     std::shared_ptr<const muon::PlanStore> plan;
     TRY(muon::get_plan(descs, n, MUON_GEMM_BF16_MFMA, stream, &plan, &st));
     const muon::PlanView& p = muon::view_of(*plan);
-    TRY_HIP(muon::launch_front(p, grads, momentum, u_out, nullptr, beta, nesterov, stream),
-            "front");
+    const muon::Hyper h{nullptr, 0.f, 0.f, beta, nesterov};
+    TRY_HIP(muon::launch_front(p, grads, momentum, u_out, nullptr, h, stream), "front");
     return MUON_OK;
 }
 
@@ -220,7 +263,7 @@ int muon_orthogonalize(const float* u, float* o_out, int64_t n_elems,
     float* partial = reinterpret_cast<float*>(ws + p.ws.partial);
     float* inv = reinterpret_cast<float*>(ws + p.ws.inv);
     if (ns_steps > 0) {
-        TRY_HIP(muon::launch_front_cast(p, nullptr, nullptr, u, 0.f, 0, ws, partial, stream),
+        TRY_HIP(muon::launch_front_cast(p, nullptr, nullptr, u, muon::Hyper{}, ws, partial, stream),
                 "sum of squares and cast");
         TRY_HIP(muon::launch_norm(p, partial, inv, true, stream), "norm");
         TRY_HIP(muon::launch_newton_schulz(p, ws, o_out, nullptr, ns_steps, stream), "newton-schulz");
@@ -251,9 +294,8 @@ int muon_apply(void* params, int param_dtype, int64_t n_param_elems, const float
     TRY(muon::check_no_alias(ranges, 2, &st));
     std::shared_ptr<const muon::PlanStore> plan;
     TRY(muon::get_plan(descs, n, MUON_GEMM_BF16_MFMA, stream, &plan, &st));
-    volatile float lrwd = lr * weight_decay;
-    const float decay = 1.0f - lrwd;
-    TRY_HIP(muon::launch_apply(muon::view_of(*plan), params, param_dtype, updates, decay, lr,
+    const muon::Hyper h{nullptr, lr, weight_decay, 0.f, 0};
+    TRY_HIP(muon::launch_apply(muon::view_of(*plan), params, param_dtype, updates, h, nullptr,
                                stream),
             "apply");
     return MUON_OK;

@@ -33,6 +33,7 @@ constexpr size_t kWsAlign = 256;
 constexpr int64_t kMaxSide = int64_t(1) << 20;
 constexpr int64_t kMaxNumel = int64_t(1) << 34;
 constexpr int kMaxNsSteps = 64;
+constexpr int kMaxGroups = 65536;  // optimizer groups per muon_step_grouped call
 
 // Quintic Newton-Schulz coefficients and the norm epsilon.
 constexpr float kNsA = 3.4445f;
@@ -60,7 +61,8 @@ struct alignas(16) MatInfo {
     int32_t chunk_begin, n_chunks;  // elementwise chunks / partial-sum slots
     int32_t cast_begin, n_cast;     // normalize/cast tiles
     float scale;        // (float) sqrt(max(1, R/C))
-    int32_t pad_[3];
+    int32_t group;      // optimizer group (muon_step_grouped), else 0
+    int32_t pad_[2];
 };
 static_assert(sizeof(MatInfo) == 128, "MatInfo layout");
 
@@ -113,8 +115,9 @@ struct Status {
     char msg[512];
 };
 
-// Shapes, shard geometry and reserved fields of every descriptor.
-int check_desc_shapes(const muon_matrix_desc_t* d, int64_t n, Status* st);
+// Shapes, shard geometry and group fields (0 <= group < n_groups) of every descriptor.
+int check_desc_shapes(const muon_matrix_desc_t* d, int64_t n, Status* st,
+                      int64_t n_groups = 1);
 // Matrices inside [0, n_elems) of the float32 state layout, 16-byte aligned,
 // pairwise disjoint.
 int check_state_ranges(const muon_matrix_desc_t* d, int64_t n, int64_t n_elems, const char* what,
@@ -164,9 +167,19 @@ class LaunchTimer {
 
 // ------------------------------------------------------------------ kernels
 
+// Optimizer hyperparameters of a launch: one set for every matrix
+// (groups == nullptr), or per matrix groups[MatInfo::group], read from device
+// memory by the kernels.
+struct Hyper {
+    const muon_group_t* groups;
+    float lr, weight_decay, beta;
+    int nesterov;
+};
+
+
 // Momentum + orthogonalization input (+ per-chunk sum of squares of U).
 hipError_t launch_front(const PlanView& p, const float* grads, float* momentum, float* u,
-                        float* partial, float beta, int nesterov, hipStream_t s);
+                        float* partial, const Hyper& h, hipStream_t s);
 // Per-chunk sum of squares of an existing U.
 hipError_t launch_sumsq(const PlanView& p, const float* u, float* partial, hipStream_t s);
 // Per-matrix 1 / (sqrt(sum of partials) + eps); partials per elementwise chunk,
@@ -179,7 +192,7 @@ hipError_t launch_norm(const PlanView& p, const float* partial, float* inv, bool
 // padding) and the per-tile sums of squares of U.  The Newton-Schulz iteration
 // 0 then applies 1 / ||U|| (launch_newton_schulz with the norm folded).
 hipError_t launch_front_cast(const PlanView& p, const float* grads, float* momentum,
-                             const float* u, float beta, int nesterov, void* ws, float* partial,
+                             const float* u, const Hyper& h, void* ws, float* partial,
                              hipStream_t s);
 // X0 = cast(U * inv) in NS orientation into the first X region, zero
 // padding; when o_direct is non-null (ns_steps == 0) write O = s * X0 there
@@ -187,11 +200,13 @@ hipError_t launch_front_cast(const PlanView& p, const float* grads, float* momen
 hipError_t launch_cast(const PlanView& p, const float* u, const float* inv, void* ws,
                        float* o_direct, hipStream_t s);
 // The decay-and-update of the apply phase, for the last Newton-Schulz
-// iteration to perform in place of storing O.
+// iteration to perform in place of storing O.  model_copy (float32 params
+// only, may be null) receives every updated weight rounded to bfloat16.
 struct FusedApply {
     void* params;
     int param_dtype;
-    float decay, lr;
+    Hyper hyper;
+    uint16_t* model_copy;
 };
 // ns_steps >= 1 Newton-Schulz iterations on the first iterate that
 // launch_front_cast stored (U unnormalized; iteration 0 scales its products by
@@ -201,8 +216,9 @@ struct FusedApply {
 // stored).
 hipError_t launch_newton_schulz(const PlanView& p, void* ws, float* o, const FusedApply* fuse,
                                 int ns_steps, hipStream_t s);
-// W <- fl(fl(W*f) - fl(lr*O)) scattered into the slices.
+// W <- fl(fl(W*f) - fl(lr*O)) scattered into the slices (and, with
+// model_copy, its bfloat16 rounding into the copy).
 hipError_t launch_apply(const PlanView& p, void* params, int param_dtype, const float* o,
-                        float decay, float lr, hipStream_t s);
+                        const Hyper& h, uint16_t* model_copy, hipStream_t s);
 
 }  // namespace muon

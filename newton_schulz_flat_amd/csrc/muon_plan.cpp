@@ -76,6 +76,7 @@ Geometry build_geometry(const muon_matrix_desc_t* d, int64_t n, int gemm_mode) {
         m.rp = int32_t(round_up(m.r, m.tile));
         m.cp = int32_t(round_up(m.c, m.tile));
         m.scale = float(std::sqrt(std::max(1.0, double(m.R) / double(m.C))));
+        m.group = d[i].group;
         // Every region start stays 256-byte aligned: rp and cp are multiples of 64.
         m.x_off = x_elems;
         x_elems += int64_t(m.rp) * m.cp;

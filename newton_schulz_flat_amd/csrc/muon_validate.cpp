@@ -24,7 +24,7 @@ static int fail(Status* st, int code, const char* fmt, ...) {
     return code;
 }
 
-int check_desc_shapes(const muon_matrix_desc_t* d, int64_t n, Status* st) {
+int check_desc_shapes(const muon_matrix_desc_t* d, int64_t n, Status* st, int64_t n_groups) {
     if (n < 0) return fail(st, MUON_ERR_BAD_ARG, "descriptor count n = %lld < 0", (long long)n);
     if (n > 0 && d == nullptr) return fail(st, MUON_ERR_NULL_POINTER, "descs is NULL");
     if (n > (int64_t(1) << 24))
@@ -37,9 +37,9 @@ int check_desc_shapes(const muon_matrix_desc_t* d, int64_t n, Status* st) {
         if (m.rows > kMaxSide || m.cols > kMaxSide || m.rows * m.cols > kMaxNumel)
             return fail(st, MUON_ERR_BAD_SHAPE, "descs[%lld]: shape %lld x %lld is too large",
                         (long long)i, (long long)m.rows, (long long)m.cols);
-        if (m.reserved != 0)
-            return fail(st, MUON_ERR_BAD_ARG, "descs[%lld]: reserved field is %d, must be 0",
-                        (long long)i, m.reserved);
+        if (m.group < 0 || m.group >= n_groups)
+            return fail(st, MUON_ERR_BAD_ARG, "descs[%lld]: group %d outside [0, %lld)",
+                        (long long)i, m.group, (long long)n_groups);
         if (m.n_shards < 1)
             return fail(st, MUON_ERR_BAD_SHAPE, "descs[%lld]: n_shards = %d < 1", (long long)i,
                         m.n_shards);

@@ -153,15 +153,15 @@ def test_step_rejects(lib, kwargs, code):
     ([(0, 8, 8, 0), (64, 8, 8, 32)], {}, "OVERLAP"),       # param ranges overlap
     ([(0, 8, 8, 0, 32, 2), (64, 4, 4, 40)], {}, "OVERLAP"),  # slice vs matrix
     ([(0, 8, 8, 0, 1 << 20, 2)], {}, "OUT_OF_BOUNDS"),     # slice 1 beyond params
-    ([(0, 8, 8, 0, 0, 0, 1)], {}, "BAD_ARG"),              # reserved != 0
+    ([(0, 8, 8, 0, 0, 0, 1)], {}, "BAD_ARG"),              # group != 0 outside muon_step_grouped
 ])
 def test_step_rejects_descriptors(lib, items, kw, code):
     arrs = []
     for it in items:
         arrs.append(it)
-    if len(items[0]) == 7:  # reserved field set by hand
+    if len(items[0]) == 7:  # group field set by hand
         arr = nsf.descs_array([items[0][:6]])
-        arr[0].reserved = items[0][6]
+        arr[0].group = items[0][6]
         rc = lib.muon_step(P, 0, 1 << 20, G, M, 1 << 20, arr, 1, 0.02, 0.01, 0.95, 1, 5, 0, W,
                            BIG, None)
     else:
@@ -196,3 +196,45 @@ def test_binding_refuses_cpu_tensors(lib):
     t = torch.zeros(64 * 32)
     with pytest.raises((ValueError, TypeError)):
         nsf.muon_step(t, t, t, [GOOD], 0.02, 0.01, 0.95)
+
+
+# ------------------------------------------------------------ muon_step_grouped
+
+GR = 0x50_0000_0000   # fake device address of a group table
+CP = 0x60_0000_0000   # fake device address of a bf16 model copy
+
+
+def grouped(lib, items, *, params=P, dtype=0, n_param=1 << 20, copy=None, grads=G, momentum=M,
+            n_state=1 << 20, groups=GR, n_groups=2, ns=5, mode=0, ws=W, ws_size=BIG):
+    arr, n = descs(*items)
+    return lib.muon_step_grouped(params, dtype, n_param, copy, grads, momentum, n_state, arr, n,
+                                 groups, n_groups, ns, mode, ws, ws_size, None)
+
+
+@pytest.mark.parametrize("items,kw,code", [
+    ([(0, 8, 8, 0, 0, 1, 2)], {}, "BAD_ARG"),                   # group 2 of 2
+    ([(0, 8, 8, 0, 0, 1, -1)], {}, "BAD_ARG"),                  # negative group
+    ([(0, 8, 8)], dict(n_groups=0), "BAD_ARG"),
+    ([(0, 8, 8)], dict(n_groups=65537), "BAD_ARG"),
+    ([(0, 8, 8)], dict(groups=None), "NULL_POINTER"),
+    ([(0, 8, 8)], dict(dtype=1, copy=CP), "BAD_ARG"),           # model copy needs f32 params
+    ([(0, 8, 8)], dict(copy=CP + 8), "MISALIGNED"),
+    ([(0, 8, 8)], dict(copy=P + 64), "ALIAS"),                  # copy inside params
+    ([(0, 8, 8)], dict(groups=G + 64), "ALIAS"),                # group table inside grads
+    ([(0, 8, 8)], dict(ns=65), "BAD_ARG"),
+    ([(0, 8, 8)], dict(ws_size=16), "WORKSPACE_TOO_SMALL"),
+])
+def test_grouped_rejects(lib, items, kw, code):
+    assert grouped(lib, items, **kw) == ERR[code], lib.muon_last_error()
+    assert lib.muon_last_error() != b""
+
+
+def test_grouped_accepts_groups_in_workspace_sizing(lib):
+    # the workspace does not depend on groups: any group index >= 0 is sized
+    assert ws_bytes(lib, [(0, 64, 32, 0, 0, 1, 7)]) == ws_bytes(lib, [(0, 64, 32)])
+    assert ws_bytes(lib, [(0, 64, 32, 0, 0, 1, -1)])[0] == ERR["BAD_ARG"]
+
+
+def test_grouped_no_matrices_is_a_noop(lib):
+    assert grouped(lib, [], params=None, grads=None, momentum=None, groups=None, ws=None,
+                   ws_size=0) == 0

@@ -51,6 +51,7 @@ class Desc:
     param_offset: int
     shard_stride: int = 0
     n_shards: int = 1
+    group: int = 0          # optimizer group (muon_step_grouped)
 
 
 @dataclass
