@@ -1,6 +1,7 @@
 """Benchmark of the MI355X Muon step (one GPU).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload llama] [--mode bf16]
+                    [--variant step|grouped|graph|master]
 
 One "step" is one whole ``muon_step`` call (momentum + Nesterov input,
 Frobenius normalization, 5 Newton-Schulz iterations, decay + apply) over the
@@ -8,6 +9,12 @@ workload's matrices, with every input already resident in HBM.  The default
 workload is one Llama-style decoder layer (Wq 4096x4096, Wk/Wv 1024x4096,
 Wo 4096x4096, gate/up 14336x4096, down 4096x14336; bfloat16 weights, float32
 gradients and momentum; synthetic seeded values).
+
+Variants (same workload): ``grouped`` runs muon_step_grouped with two optimizer
+groups (attention and MLP matrices, different lr / weight decay / beta) read
+from a device table; ``graph`` captures that grouped step in a HIP graph and
+times graph replays; ``master`` keeps float32 master weights and refreshes a
+bfloat16 model copy in the same step.
 
 Prints one JSON line: matrices/s for the whole step, the Newton-Schulz
 algorithmic TFLOP/s and its fraction of the bf16 dense MFMA peak, the roofline
@@ -123,6 +130,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama", choices=wlm.WORKLOADS)
     ap.add_argument("--mode", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--variant", default="step", choices=["step", "grouped", "graph", "master"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (calibrates the "
@@ -151,16 +159,44 @@ def main():
         build.build()
     nsf.load_library()
 
+    import dataclasses
     h = wlm.HYPER
     wl = wlm.make_workload(args.workload)
+    if args.variant == "master":
+        wl = dataclasses.replace(wl, param_dtype="f32")
     torch.cuda.set_device(0)
     params, grads, mom = wlm.make_tensors(wl, "cuda:0")
-    ws = nsf.workspace_for(wl.descs, args.mode, grads.device)
+    descs = wl.descs
+    if args.variant in ("grouped", "graph"):
+        # attention matrices (q, k, v, o) in group 0, the rest (MLP) in group 1
+        descs = [dataclasses.replace(d, group=0 if nm in ("wq", "wk", "wv", "wo") else 1)
+                 for d, nm in zip(wl.descs, wl.names)]
+        table = nsf.group_table([(h["lr"], h["weight_decay"], h["beta"], True),
+                                 (0.5 * h["lr"], 0.1, 0.9, True)], "cuda:0")
+    elif args.variant == "master":
+        table = nsf.group_table([(h["lr"], h["weight_decay"], h["beta"], True)], "cuda:0")
+        model_copy = params.to(torch.bfloat16)
+    ws = nsf.workspace_for(descs, args.mode, grads.device)
 
-    def step():
-        nsf.muon_step(params, grads, mom, wl.descs, h["lr"], h["weight_decay"], h["beta"],
-                      nesterov=h["nesterov"], ns_steps=h["ns_steps"], mode=args.mode,
-                      workspace=ws)
+    def eager():
+        if args.variant == "step":
+            nsf.muon_step(params, grads, mom, descs, h["lr"], h["weight_decay"], h["beta"],
+                          nesterov=h["nesterov"], ns_steps=h["ns_steps"], mode=args.mode,
+                          workspace=ws)
+        else:
+            nsf.muon_step_grouped(params, grads, mom, descs, table, ns_steps=h["ns_steps"],
+                                  mode=args.mode, workspace=ws,
+                                  model_copy=model_copy if args.variant == "master" else None)
+
+    step = eager
+    if args.variant == "graph":
+        eager()  # builds the plan outside capture
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            eager()
+        torch.cuda.synchronize()
+        step = graph.replay
 
     for _ in range(args.warmup):
         step()
@@ -168,7 +204,7 @@ def main():
 
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    nsf.muon_profile_begin()
+    nsf.muon_profile_begin()   # replays of a graph are not bracketed: no kernel table
     torch.cuda.synchronize()
     ev0.record(stream)
     for _ in range(args.steps):
@@ -179,38 +215,40 @@ def main():
     ms = ev0.elapsed_time(ev1) / args.steps
 
     fl = stage_flops(wl, h["ns_steps"])
-    ns_ms = sum(v[0] for k, v in kernels.items() if k.startswith("ns_")) / args.steps
     ns_alg = sum(fl.values()) * h["ns_steps"]
-    ns_tflops = ns_alg / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else 0.0
     ew = elementwise_bytes(wl, args.mode)
-
-    # dominant kernel = largest total time; its algorithmic work per launch
-    name, (tot_ms, launches) = max(kernels.items(), key=lambda kv: kv[1][0])
-    avg_s = tot_ms / launches * 1e-3
-    if name.startswith("ns_"):
-        stage = name.split("_")[1]
-        same = [k for k in kernels if k.startswith(f"ns_{stage}_")]
-        if len(same) == 1:
-            work = fl[stage]
-        else:  # several tile sizes: attribute this stage's flops by measured time share
-            work = fl[stage] * tot_ms / sum(kernels[k][0] for k in same)
-        roof = {"kernel": name, "bound": "mfma", "achieved": work / avg_s / 1e12,
-                "peak": PEAK_TFLOPS[args.mode], "unit": "TFLOP/s",
-                "work_per_launch": work, "avg_launch_ms": avg_s * 1e3}
-    else:
-        work = ew.get(name, 0)
-        roof = {"kernel": name, "bound": "hbm", "achieved": work / avg_s / 1e9,
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "work_per_launch": work,
-                "avg_launch_ms": avg_s * 1e3}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = recorded_traffic(name, "llama_layer" if wl.name == "llama" else wl.name)
-
-    per_kernel = {k: {"ms_per_step": v[0] / args.steps, "launches_per_step": v[1] / args.steps}
-                  for k, v in sorted(kernels.items())}
-    for k in ("front_cast", "front", "cast", "apply"):
-        if k in kernels:
-            per_kernel[k]["GB/s"] = ew[k] / (kernels[k][0] / kernels[k][1] * 1e-3) / 1e9
-            per_kernel[k]["frac_hbm"] = per_kernel[k]["GB/s"] / PEAK_HBM_GBS
+    ns_ms, ns_tflops, roof, per_kernel = None, None, None, {}
+    if kernels:  # eager launches (graph replays carry no per-kernel events)
+        ns_ms = sum(v[0] for k, v in kernels.items() if k.startswith("ns_")) / args.steps
+        ns_tflops = ns_alg / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else 0.0
+        # dominant kernel = largest total time; its algorithmic work per launch
+        name, (tot_ms, launches) = max(kernels.items(), key=lambda kv: kv[1][0])
+        avg_s = tot_ms / launches * 1e-3
+        if name.startswith("ns_"):
+            stage = name.split("_")[1]
+            same = [k for k in kernels if k.startswith(f"ns_{stage}_")]
+            if len(same) == 1:
+                work = fl[stage]
+            else:  # several tile sizes: attribute this stage's flops by measured time share
+                work = fl[stage] * tot_ms / sum(kernels[k][0] for k in same)
+            roof = {"kernel": name, "bound": "mfma", "achieved": work / avg_s / 1e12,
+                    "peak": PEAK_TFLOPS[args.mode], "unit": "TFLOP/s",
+                    "work_per_launch": work, "avg_launch_ms": avg_s * 1e3}
+        else:
+            work = ew.get(name, 0)
+            roof = {"kernel": name, "bound": "hbm", "achieved": work / avg_s / 1e9,
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "work_per_launch": work,
+                    "avg_launch_ms": avg_s * 1e3}
+        roof["frac"] = roof["achieved"] / roof["peak"]
+        roof["traffic"] = (recorded_traffic(name, "llama_layer" if wl.name == "llama" else wl.name)
+                           if args.variant == "step" else None)
+        per_kernel = {k: {"ms_per_step": v[0] / args.steps,
+                          "launches_per_step": v[1] / args.steps}
+                      for k, v in sorted(kernels.items())}
+        for k in ("front_cast", "front", "cast", "apply"):
+            if k in kernels:
+                per_kernel[k]["GB/s"] = ew[k] / (kernels[k][0] / kernels[k][1] * 1e-3) / 1e9
+                per_kernel[k]["frac_hbm"] = per_kernel[k]["GB/s"] / PEAK_HBM_GBS
 
     out = {
         "metric": METRIC,
@@ -229,9 +267,9 @@ def main():
                    "matrices": wl.n, "elements": wl.numel(), "param_dtype": wl.param_dtype,
                    "gemm_mode": args.mode, "ns_steps": h["ns_steps"], "lr": h["lr"],
                    "weight_decay": h["weight_decay"], "beta": h["beta"], "nesterov": True,
-                   "parallelism": "single-gpu"},
+                   "parallelism": "single-gpu", "variant": args.variant},
         "ns_tflops": ns_tflops,
-        "ns_frac_of_peak": ns_tflops / PEAK_TFLOPS[args.mode],
+        "ns_frac_of_peak": None if ns_tflops is None else ns_tflops / PEAK_TFLOPS[args.mode],
         "ns_ms_per_step": ns_ms,
         "roofline": roof,
         "kernels": per_kernel,
