@@ -395,46 +395,64 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
     //                registers); after step 2 all waves meet at the barrier,
     //                after which this block's LDS buffer is free;
     //   q = 3:       the MFMAs run on fragments already in registers while the
-    //                fragments of step 0 of the next block are read, block
-    //                kb + 2 (in registers since step 3 of the previous block)
-    //                is written into the freed buffer, and the global loads of
-    //                block kb + 3 are issued.
-    // A global load thus has one whole K block to arrive before it is
-    // consumed, and step 3's MFMAs give the matrix pipe work while every wave
-    // refills its fragments.  Blocks past the end reload the last block
-    // (valid, unused copies) so the loop stays branch free.
+    //                fragments of step 0 of the next block are read.
+    // Staging: each step writes one share of the staged registers into LDS --
+    // step 3 into the freed buffer (block kb + 2), steps 0-2 into the other one
+    // (completing block kb + 1 before the barrier) -- and reloads those
+    // registers right away, so a global load has one whole K block to arrive
+    // and the LDS writes and loads are spread evenly over the steps.  Step 3's
+    // MFMAs give the matrix pipe work while every wave refills its fragments.
+    // Blocks past the end reload the last block (valid, unused copies) so the
+    // loop stays branch free.
     const int nkb = K / kBk;
     constexpr int kMfma = kMi * kNj;  // MFMAs per step q (per K sub-step for bf16)
     auto q_off = [&](int blk) -> int64_t {
         return (kTransQ || kQLdsT) ? int64_t(blk) * kBk * cp : int64_t(blk) * kBk;
     };
+    // Staged register pair l (pa[l], pb[l]) is written to LDS and reloaded at
+    // step (3 + l / kPerStep) mod 4, so that every step carries the same share of
+    // LDS writes and global loads.  (The register-transposed Q of float32 stage X
+    // reads every pb in each write: there all pairs are handled at step 3.)
+    constexpr int kPerStep = kTransQ ? kL : (kL + 3) / 4;
     u32x4 pa[kL], pb[kL];
     {
-        // blocks 0 and 1 into both LDS buffers, block 2 into the registers
+        // block 0 into LDS buffer 0; block 1 into buffer 1 for the pairs handled
+        // at step 3 (those are reloaded with block 2), the rest stay in registers
+        // and are written during steps 0-2 of block 0
         u32x4 pa1[kL], pb1[kL];
         const int b1 = nkb > 1 ? 1 : 0, b2 = nkb > 2 ? 2 : nkb - 1;
 #pragma unroll
         for (int l = 0; l < kL; ++l) {
-            pa[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep);
-            pb[l] = *reinterpret_cast<const u32x4*>(gq + l * qstep);
+            pa1[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep);
+            pb1[l] = *reinterpret_cast<const u32x4*>(gq + l * qstep);
         }
 #pragma unroll
         for (int l = 0; l < kL; ++l) {
-            pa1[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep + int64_t(b1) * kBk);
-            pb1[l] = *reinterpret_cast<const u32x4*>(gq + l * qstep + q_off(b1));
+            pa[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep + int64_t(b1) * kBk);
+            pb[l] = *reinterpret_cast<const u32x4*>(gq + l * qstep + q_off(b1));
         }
 #pragma unroll
-        for (int l = 0; l < kL; ++l) *reinterpret_cast<u32x4*>(lds + lds_st + l * kLdsPass) = pa[l];
+        for (int l = 0; l < kL; ++l) *reinterpret_cast<u32x4*>(lds + lds_st + l * kLdsPass) = pa1[l];
 #pragma unroll
-        for (int w = 0; w < kQW; ++w) store_q<kTransQ, kL>(lds + q_st, pb, w, q_pass);
+        for (int w = 0; w < kQW; ++w) store_q<kTransQ, kL>(lds + q_st, pb1, w, q_pass);
+        if constexpr (kTransQ) {
 #pragma unroll
-        for (int l = 0; l < kL; ++l) *reinterpret_cast<u32x4*>(lds + kBuf + lds_st + l * kLdsPass) = pa1[l];
+            for (int l = 0; l < kL; ++l) *reinterpret_cast<u32x4*>(lds + kBuf + lds_st + l * kLdsPass) = pa[l];
 #pragma unroll
-        for (int w = 0; w < kQW; ++w) store_q<kTransQ, kL>(lds + kBuf + q_st, pb1, w, q_pass);
+            for (int w = 0; w < kQW; ++w) store_q<kTransQ, kL>(lds + kBuf + q_st, pb, w, q_pass);
 #pragma unroll
-        for (int l = 0; l < kL; ++l) {
-            pa[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep + int64_t(b2) * kBk);
-            pb[l] = *reinterpret_cast<const u32x4*>(gq + l * qstep + q_off(b2));
+            for (int l = 0; l < kL; ++l) {
+                pa[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep + int64_t(b2) * kBk);
+                pb[l] = *reinterpret_cast<const u32x4*>(gq + l * qstep + q_off(b2));
+            }
+        } else {
+#pragma unroll
+            for (int l = 0; l < kPerStep && l < kL; ++l) {
+                *reinterpret_cast<u32x4*>(lds + kBuf + lds_st + l * kLdsPass) = pa[l];
+                *reinterpret_cast<u32x4*>(lds + kBuf + q_st + l * q_pass) = pb[l];
+                pa[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep + int64_t(b2) * kBk);
+                pb[l] = *reinterpret_cast<const u32x4*>(gq + l * qstep + q_off(b2));
+            }
         }
     }
     __syncthreads();
@@ -448,15 +466,22 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
         fb[0][j] = kQLdsT ? read_tr(lds + fbt_off + j * 64, 4 * kS)
                           : *reinterpret_cast<const u32x4*>(lds + fb_off + j * 32 * kLdsStride);
     for (int kb = 0; kb < nkb; ++kb) {
-        const int b3 = kb + 3 < nkb ? kb + 3 : nkb - 1;  // block loaded during step 3
+        // steps 0-2 complete block kb + 1 in the other buffer and load block kb + 2;
+        // step 3 starts block kb + 2 in this (now free) buffer and loads block kb + 3
+        const int b2 = kb + 2 < nkb ? kb + 2 : nkb - 1;
+        const int b3 = kb + 3 < nkb ? kb + 3 : nkb - 1;
+        const int64_t k2 = int64_t(b2) * kBk, qk2 = q_off(b2);
         const int64_t k3 = int64_t(b3) * kBk, qk3 = q_off(b3);
         unsigned char* buf = lds + (kb & 1) * kBuf;
-        const unsigned char* nbuf = lds + ((kb + 1) & 1) * kBuf;
+        unsigned char* nbuf = lds + ((kb + 1) & 1) * kBuf;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int cur = q & 1;
             const unsigned char* rbuf = q < 3 ? buf : nbuf;
             const int rq = q < 3 ? q + 1 : 0;
+            unsigned char* wbuf = q == 3 ? buf : nbuf;
+            const int64_t kk = q == 3 ? k3 : k2, qkk = q == 3 ? qk3 : qk2;
+            const int l0 = ((q + 1) & 3) * kPerStep;  // first pair of this step
 #pragma unroll
             for (int m = 0; m < kMfma; ++m) {
                 const int i = m / kNj, j = m % kNj;
@@ -483,24 +508,40 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                         fb[cur ^ 1][rd - kMi] = *reinterpret_cast<const u32x4*>(
                             rbuf + fb_off + (rd - kMi) * 32 * kLdsStride + rq * 16);
                 }
-                if (q == 3) {
-                    // this block's buffer is free: block kb + 2 goes in, then block kb + 3 is loaded
+                if constexpr (kTransQ) {
+                    if (q == 3) {
+                        // this block's buffer is free: block kb + 2 goes in, then block kb + 3
+                        // is loaded (pa right after its write; pb after all writes, below)
 #pragma unroll
-                    for (int l = m; l < kL + kQW; l += kMfma) {
-                        if (l < kL)
-                            *reinterpret_cast<u32x4*>(buf + lds_st + l * kLdsPass) = pa[l];
-                        else
-                            store_q<kTransQ, kL>(buf + q_st, pb, l - kL, q_pass);
-                    }
-                    // a register is reloaded right after the write that consumed it;
-                    // the register-transposed Q writes read every pb, so those reloads
-                    // wait until all writes are issued (below)
+                        for (int l = m; l < kL + kQW; l += kMfma) {
+                            if (l < kL)
+                                *reinterpret_cast<u32x4*>(buf + lds_st + l * kLdsPass) = pa[l];
+                            else
+                                store_q<kTransQ, kL>(buf + q_st, pb, l - kL, q_pass);
+                        }
 #pragma unroll
-                    for (int l = m; l < (kTransQ ? kL : 2 * kL); l += kMfma) {
-                        if (l < kL)
+                        for (int l = m; l < kL; l += kMfma)
                             pa[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep + k3);
-                        else
-                            pb[l - kL] = *reinterpret_cast<const u32x4*>(gq + (l - kL) * qstep + qk3);
+                    }
+                } else {
+                    // this step's pairs: writes first, then the reloads
+#pragma unroll
+                    for (int it = m; it < 4 * kPerStep; it += kMfma) {
+                        const int l = l0 + (it % (2 * kPerStep)) / 2;
+                        const bool is_q = (it & 1) != 0;
+                        if (l < kL) {
+                            if (it < 2 * kPerStep) {
+                                if (is_q)
+                                    *reinterpret_cast<u32x4*>(wbuf + q_st + l * q_pass) = pb[l];
+                                else
+                                    *reinterpret_cast<u32x4*>(wbuf + lds_st + l * kLdsPass) = pa[l];
+                            } else {
+                                if (is_q)
+                                    pb[l] = *reinterpret_cast<const u32x4*>(gq + l * qstep + qkk);
+                                else
+                                    pa[l] = *reinterpret_cast<const u32x4*>(gp + l * rstep + kk);
+                            }
+                        }
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
