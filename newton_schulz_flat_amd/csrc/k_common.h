@@ -33,6 +33,18 @@ __device__ __forceinline__ uint16_t bf16_rne(float x) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
 
+// 16-byte loads and stores of data that is touched once per pass (optimizer
+// state streams): nontemporal, so that they do not displace cached operands.
+typedef float f32x4_stream __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load4_stream(const float* p) {
+    const f32x4_stream t = __builtin_nontemporal_load(reinterpret_cast<const f32x4_stream*>(p));
+    return make_float4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ void store4_stream(float* p, float4 v) {
+    const f32x4_stream t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<f32x4_stream*>(p));
+}
+
 // One matrix's optimizer scalars; decay = fl(1 - fl(lr * wd)), the same two
 // roundings as on the host.
 struct HyperVals {

@@ -5,14 +5,18 @@
 // squares (per elementwise chunk, or per 64 x 64 tile) in a fixed order and
 // stores inv = 1 / (sqrt(sum) + 1e-7).
 //
-// front_cast_kernel: one workgroup per 64 x 64 tile of the padded
-// NS-orientation matrix (the tiles of cast_kernel).  It reads the matching
-// block of G and M (or of U) along U's rows, computes M <- fl(fl(beta M) + G)
-// (stored) and U = fl(fl(beta M) + G) (or M) in float32 exactly as the
-// elementwise front kernel does, stores U rounded to the Newton-Schulz type --
-// not yet divided by its norm: the first iteration applies 1 / ||U|| in its
-// float32 epilogues -- in NS orientation, and writes the tile's sum of squares
-// of U (fixed order) for norm_kernel.  One pass replaces front + cast.
+// front_cast_kernel: one workgroup per 4096 elements of the padded
+// NS-orientation matrix (as many workgroups as cast_kernel has 64 x 64 tiles).
+// It reads the matching elements of G and M (or of U) along U's rows,
+// computes M <- fl(fl(beta M) + G) (stored) and U = fl(fl(beta M) + G) (or M)
+// in float32 exactly as the elementwise front kernel does, stores U rounded to
+// the Newton-Schulz type -- not yet divided by its norm: the first iteration
+// applies 1 / ||U|| in its float32 epilogues -- in NS orientation, and writes
+// the workgroup's sum of squares of U (fixed order) for norm_kernel.  A wide or
+// square matrix keeps its orientation, and each workgroup streams a contiguous
+// run of the padded iterate; a tall one is handled in 64 x 64 tiles transposed
+// through LDS.  G and M are streamed with nontemporal accesses.  One pass
+// replaces front + cast.
 //
 // cast_kernel: one workgroup per 64 x 64 tile of the padded NS-orientation
 // matrix X0 (rp x cp).  It reads the matching 64 x 64 block of U in U's own
@@ -122,68 +126,95 @@ __global__ __launch_bounds__(256) void front_cast_kernel(const MatInfo* __restri
                                                          TX* __restrict__ x,
                                                          float* __restrict__ partial) {
     constexpr int T = kCastTile;
+    constexpr int kIters = T * T / 4 / 256;  // 4-element groups per thread
     __shared__ float tile[T][T + 1];
     __shared__ float wsum[4];
     const int blk = blockIdx.x;
     const int mi = owner_of(prefix, n, blk);
     const MatInfo& mt = mats[mi];
     const int t = blk - mt.cast_begin;
-    const int ntj = mt.cp / T;
-    const int ti = t / ntj, tj = t % ntj;
     const bool tall = mt.tall != 0;
-    // Tile origin in U's own (R x C) coordinates.
-    const int ur0 = tall ? tj * T : ti * T;
-    const int uc0 = tall ? ti * T : tj * T;
     const bool vec = (mt.C & 3) == 0;  // rows start 16-byte aligned
     const HyperVals hv = hyper_for(h, mt);
     const float beta = hv.beta;
     const int nesterov = hv.nesterov;
-    float ss = 0.f;
-    // 64 rows x 16 four-element segments; 16 consecutive threads cover one row
-#pragma unroll
-    for (int it = 0; it < T * T / 4 / 256; ++it) {
-        const int seg = it * 256 + int(threadIdx.x);
-        const int rr = seg >> 4, c4 = (seg & 15) * 4;
-        const int gr = ur0 + rr, gc = uc0 + c4;
-        float uv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (gr < mt.R && gc < mt.C) {
-            const int64_t e = mt.off + int64_t(gr) * mt.C + gc;
-            if (vec && gc + 3 < mt.C) {
-                if (kStep) {
-                    const float4 gv = *reinterpret_cast<const float4*>(g + e);
-                    const float4 mv = *reinterpret_cast<const float4*>(m + e);
-                    const float g4[4] = {gv.x, gv.y, gv.z, gv.w};
-                    const float m4[4] = {mv.x, mv.y, mv.z, mv.w};
-                    float m1[4];
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        m1[q] = beta * m4[q] + g4[q];
-                        uv[q] = nesterov ? beta * m1[q] + g4[q] : m1[q];
-                    }
-                    *reinterpret_cast<float4*>(m + e) = make_float4(m1[0], m1[1], m1[2], m1[3]);
-                } else {
-                    const float4 q4 = *reinterpret_cast<const float4*>(u_in + e);
-                    uv[0] = q4.x, uv[1] = q4.y, uv[2] = q4.z, uv[3] = q4.w;
-                }
-            } else {
+    // U at 4 consecutive elements of U's row gr from column gc (zero outside
+    // R x C); with kStep, M is updated there.
+    auto front4 = [&](int gr, int gc, float uv[4]) {
+        uv[0] = uv[1] = uv[2] = uv[3] = 0.f;
+        if (gr >= mt.R || gc >= mt.C) return;
+        const int64_t e = mt.off + int64_t(gr) * mt.C + gc;
+        if (vec && gc + 3 < mt.C) {
+            if (kStep) {
+                const float4 gv = load4_stream(g + e);
+                const float4 mv = load4_stream(m + e);
+                const float g4[4] = {gv.x, gv.y, gv.z, gv.w};
+                const float m4[4] = {mv.x, mv.y, mv.z, mv.w};
+                float m1[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    if (gc + q < mt.C) {
-                        if (kStep) {
-                            const float m1 = beta * m[e + q] + g[e + q];
-                            m[e + q] = m1;
-                            uv[q] = nesterov ? beta * m1 + g[e + q] : m1;
-                        } else {
-                            uv[q] = u_in[e + q];
-                        }
+                    m1[q] = beta * m4[q] + g4[q];
+                    uv[q] = nesterov ? beta * m1[q] + g4[q] : m1[q];
+                }
+                store4_stream(m + e, make_float4(m1[0], m1[1], m1[2], m1[3]));
+            } else {
+                const float4 q4 = load4_stream(u_in + e);
+                uv[0] = q4.x, uv[1] = q4.y, uv[2] = q4.z, uv[3] = q4.w;
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (gc + q < mt.C) {
+                    if (kStep) {
+                        const float m1 = beta * m[e + q] + g[e + q];
+                        m[e + q] = m1;
+                        uv[q] = nesterov ? beta * m1 + g[e + q] : m1;
+                    } else {
+                        uv[q] = u_in[e + q];
                     }
                 }
             }
         }
+    };
+    float ss = 0.f;
+    TX* xm = x + mt.x_off;
+    if (!tall) {
+        // The iterate has U's own orientation: workgroup t takes the 4096
+        // consecutive elements [4096 t, 4096 t + 4096) of the row-major rp x cp
+        // iterate (rows padded to cp), thread tid the 4-element groups
+        // it * 256 + tid, so that G, M and X stream along rows.
+        const int64_t base = int64_t(t) * (T * T);
+        const int i0 = int(base / mt.cp), j0 = int(base % mt.cp);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            tile[rr][c4 + q] = uv[q];
-            ss = ss + uv[q] * uv[q];
+        for (int it = 0; it < kIters; ++it) {
+            const int o = (it * 256 + int(threadIdx.x)) * 4;
+            const int e = j0 + o;
+            float uv[4];
+            front4(i0 + e / mt.cp, e % mt.cp, uv);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) ss = ss + uv[q] * uv[q];
+            store_x4(xm + base + o, uv);
+        }
+    } else {
+        // Tall: workgroup t takes the 64 x 64 tile (ti, tj) of the iterate, read
+        // along U's rows (64 rows x 16 four-element segments, 16 consecutive
+        // threads per row) and transposed through LDS.  Consecutive workgroups
+        // take consecutive ti, i.e. neighbouring column blocks of the same 64
+        // rows of U.
+        const int nti = mt.rp / T;
+        const int tj = t / nti, ti = t % nti;
+        const int ur0 = tj * T, uc0 = ti * T;  // tile origin in U's (R x C) coordinates
+#pragma unroll
+        for (int it = 0; it < kIters; ++it) {
+            const int seg = it * 256 + int(threadIdx.x);
+            const int rr = seg >> 4, c4 = (seg & 15) * 4;
+            float uv[4];
+            front4(ur0 + rr, uc0 + c4, uv);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                tile[rr][c4 + q] = uv[q];
+                ss = ss + uv[q] * uv[q];
+            }
         }
     }
     // deterministic block sum: fixed shuffle tree, then the 4 wave sums in order
@@ -191,15 +222,18 @@ __global__ __launch_bounds__(256) void front_cast_kernel(const MatInfo* __restri
     if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
     __syncthreads();
     if (threadIdx.x == 0) partial[blk] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
-    TX* xm = x + mt.x_off;
-    // X[i][j], i = ti*T + a, j = tj*T + b  (native element tile[a][b] or tile[b][a]);
-    // each thread writes 4 consecutive elements of a row
-    for (int idx = threadIdx.x; idx < T * T / 4; idx += 256) {
-        const int a = idx / (T / 4), b = (idx % (T / 4)) * 4;
-        float v[4];
+    if (tall) {
+        // X[i][j], i = ti*T + a, j = tj*T + b = U[j][i] = tile[b][a]; each thread
+        // writes 4 consecutive elements of a row
+        const int nti = mt.rp / T;
+        const int tj = t / nti, ti = t % nti;
+        for (int idx = threadIdx.x; idx < T * T / 4; idx += 256) {
+            const int a = idx / (T / 4), b = (idx % (T / 4)) * 4;
+            float v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = tall ? tile[b + q][a] : tile[a][b + q];
-        store_x4(xm + int64_t(ti * T + a) * mt.cp + tj * T + b, v);
+            for (int q = 0; q < 4; ++q) v[q] = tile[b + q][a];
+            store_x4(xm + int64_t(ti * T + a) * mt.cp + tj * T + b, v);
+        }
     }
 }
 
