@@ -44,6 +44,15 @@ __device__ __forceinline__ void store4_stream(float* p, float4 v) {
     const f32x4_stream t = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(t, reinterpret_cast<f32x4_stream*>(p));
 }
+typedef uint32_t u32x2_stream __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 load2_stream(const uint2* p) {
+    const u32x2_stream t = __builtin_nontemporal_load(reinterpret_cast<const u32x2_stream*>(p));
+    return make_uint2(t.x, t.y);
+}
+__device__ __forceinline__ void store2_stream(uint2* p, uint2 v) {
+    const u32x2_stream t = {v.x, v.y};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x2_stream*>(p));
+}
 
 // One matrix's optimizer scalars; decay = fl(1 - fl(lr * wd)), the same two
 // roundings as on the host.

@@ -7,7 +7,8 @@
 //
 // All three are HBM-bound streams: each workgroup owns one chunk of
 // 256 x 4 x 8 consecutive elements of one matrix and moves them with 16-byte
-// (float4) loads and stores, consecutive lanes on consecutive vectors.
+// (float4) nontemporal loads and stores, consecutive lanes on consecutive
+// vectors.
 // Floating-point contraction is off so that every multiply and add rounds on
 // its own, in the documented order (bit-exact against a same-order float32
 // reference).
@@ -54,14 +55,14 @@ __global__ __launch_bounds__(kEwThreads) void front_kernel(
         if (e + kEwVec <= end) {
             float4 uv;
             if (kMode == 0) {
-                const float4 gv = *reinterpret_cast<const float4*>(g + e);
-                const float4 mv = *reinterpret_cast<const float4*>(m + e);
+                const float4 gv = load4_stream(g + e);
+                const float4 mv = load4_stream(m + e);
                 float4 m1;
                 m1.x = beta * mv.x + gv.x;
                 m1.y = beta * mv.y + gv.y;
                 m1.z = beta * mv.z + gv.z;
                 m1.w = beta * mv.w + gv.w;
-                *reinterpret_cast<float4*>(m + e) = m1;
+                store4_stream(m + e, m1);
                 if (nesterov) {
                     uv.x = beta * m1.x + gv.x;
                     uv.y = beta * m1.y + gv.y;
@@ -70,9 +71,9 @@ __global__ __launch_bounds__(kEwThreads) void front_kernel(
                 } else {
                     uv = m1;
                 }
-                *reinterpret_cast<float4*>(u + e) = uv;
+                store4_stream(u + e, uv);
             } else {
-                uv = *reinterpret_cast<const float4*>(u + e);
+                uv = load4_stream(u + e);
             }
             ss += uv.x * uv.x;
             ss += uv.y * uv.y;
@@ -100,17 +101,15 @@ __global__ __launch_bounds__(kEwThreads) void front_kernel(
     }
 }
 
-__device__ __forceinline__ void store_w(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+__device__ __forceinline__ void store_w(float* p, float4 v) { store4_stream(p, v); }
 __device__ __forceinline__ void store_w(uint16_t* p, float4 v) {
     const uint32_t lo = uint32_t(bf16_rne(v.x)) | (uint32_t(bf16_rne(v.y)) << 16);
     const uint32_t hi = uint32_t(bf16_rne(v.z)) | (uint32_t(bf16_rne(v.w)) << 16);
-    *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+    store2_stream(reinterpret_cast<uint2*>(p), make_uint2(lo, hi));
 }
-__device__ __forceinline__ float4 load_w(const float* p) {
-    return *reinterpret_cast<const float4*>(p);
-}
+__device__ __forceinline__ float4 load_w(const float* p) { return load4_stream(p); }
 __device__ __forceinline__ float4 load_w(const uint16_t* p) {
-    const uint2 b = *reinterpret_cast<const uint2*>(p);
+    const uint2 b = load2_stream(reinterpret_cast<const uint2*>(p));
     return make_float4(__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xffff0000u),
                        __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xffff0000u));
 }
@@ -144,7 +143,7 @@ __global__ __launch_bounds__(kEwThreads) void apply_kernel(
                 const int64_t k = j / slice;
                 dst = poff + k * stride + (j - k * slice);
             }
-            const float4 ov = *reinterpret_cast<const float4*>(o + off + j);
+            const float4 ov = load4_stream(o + off + j);
             const float4 wv = load_w(w + dst);
             float4 r;
             r.x = wv.x * decay - lr * ov.x;
