@@ -406,6 +406,55 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
     // loop stays branch free.
     const int nkb = K / kBk;
     constexpr int kMfma = kMi * kNj;  // MFMAs per step q (per K sub-step for bf16)
+    // float32 products with long contractions: every kFlushBlocks K blocks the
+    // accumulators are added, in order, into this tile's own float32 output
+    // region (written by no other workgroup of the launch and read by none) and
+    // restarted, so that no accumulation chain runs over more than
+    // kFlushBlocks * 32 products -- one float32 chain over 2^20 positive terms
+    // drifts by ~5e-4 relative.  The epilogue later overwrites the region.
+    // 64- and 128-tiles only: the plan gives float32 256-tiles contractions of
+    // at most kFlushBlocks * 32 (their 256 accumulators leave no registers for
+    // this path).
+    constexpr int kFlushBlocks = 1024;
+    constexpr bool kFlush = !BF16 && TILE < 256;
+    float* sbase = nullptr;
+    int sld = 0;
+    if constexpr (kFlush) {
+        if (STAGE == kStageX) {
+            sbase = static_cast<float*>(args.x_next) + mt.x_off;
+            sld = cp;
+        } else {
+            sbase = static_cast<float*>(STAGE == kStageA ? args.ga : args.gb) + mt.g_off;
+            sld = rp;
+        }
+    }
+    const int srow0 = ti * TILE + wm * G::kWm + hk * 4, scol0 = tj * TILE + wn * G::kWn + lr;
+    // partial sums: first flush stores, later ones add (earlier segments first);
+    // fold == true adds the stored sum into the accumulators instead
+    auto flush = [&](bool first, bool fold) {
+        // opaque copies: keeps the address arithmetic on this rare path instead
+        // of hoisted (and held in registers) across the main loop
+        int ld_f = sld, row_f = srow0, col_f = scol0;
+        asm volatile("" : "+s"(ld_f));
+        asm volatile("" : "+v"(row_f), "+v"(col_f));
+        float* const b0 = sbase + int64_t(row_f) * ld_f + col_f;
+#pragma unroll
+        for (int i = 0; i < kMi; ++i)
+#pragma unroll
+            for (int j = 0; j < kNj; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    float* sp = b0 + int64_t(i * 32 + (e >> 2) * 8 + (e & 3)) * ld_f + j * 32;
+                    if (fold) {
+                        acc[i][j][e] = *sp + acc[i][j][e];
+                    } else {
+                        *sp = first ? acc[i][j][e] : *sp + acc[i][j][e];
+                        acc[i][j][e] = 0.f;
+                    }
+                    // one fragment's values in flight at a time
+                    if ((e & 15) == 15) asm volatile("" ::: "memory");
+                }
+    };
     auto q_off = [&](int blk) -> int64_t {
         return (kTransQ || kQLdsT) ? int64_t(blk) * kBk * cp : int64_t(blk) * kBk;
     };
@@ -553,6 +602,12 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
             }
             if (q == 2) __syncthreads();
         }
+        if constexpr (kFlush) {
+            if ((kb + 1) % kFlushBlocks == 0 && kb + 1 < nkb) flush(kb + 1 == kFlushBlocks, false);
+        }
+    }
+    if constexpr (kFlush) {
+        if (nkb > kFlushBlocks) flush(false, true);
     }
     // the last step read (unused) fragments: let every wave finish with LDS
     // before the epilogue reuses it

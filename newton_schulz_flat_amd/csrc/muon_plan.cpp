@@ -34,11 +34,15 @@ constexpr int kXcds = 8;  // MI355X dispatches workgroup i to XCD i % 8
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
-// GEMM tile size for a matrix whose NS orientation has r rows.  Large tiles
+// GEMM tile size for a matrix whose NS orientation is r x c.  Large tiles
 // give the MFMA pipeline the operand reuse it needs; small matrices use small
-// tiles so that zero padding stays a small fraction of the work.
-int choose_tile(int64_t r) {
-    if (r >= 768) return 256;
+// tiles so that zero padding stays a small fraction of the work.  float32
+// products longer than kF32ChainK use at most 128-tiles: only those split
+// their accumulation chains (the 256-tile has no registers to spare), and
+// every contraction of a 256-tile is then at most c.
+constexpr int64_t kF32ChainK = 32768;
+int choose_tile(int64_t r, int64_t c, int gemm_mode) {
+    if (r >= 768 && (gemm_mode != MUON_GEMM_F32 || c <= kF32ChainK)) return 256;
     if (r >= 160) return 128;
     return 64;
 }
@@ -72,7 +76,7 @@ Geometry build_geometry(const muon_matrix_desc_t* d, int64_t n, int gemm_mode) {
         m.tall = m.R > m.C;
         m.r = std::min(m.R, m.C);
         m.c = std::max(m.R, m.C);
-        m.tile = choose_tile(m.r);
+        m.tile = choose_tile(m.r, m.c, gemm_mode);
         m.rp = int32_t(round_up(m.r, m.tile));
         m.cp = int32_t(round_up(m.c, m.tile));
         m.scale = float(std::sqrt(std::max(1.0, double(m.R) / double(m.C))));

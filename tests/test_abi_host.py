@@ -79,6 +79,8 @@ def test_workspace_bytes_sizes(lib):
     ((0, 0, 5), "BAD_SHAPE"),
     ((0, 5, -1), "BAD_SHAPE"),
     ((0, 1 << 21, 4), "BAD_SHAPE"),
+    ((0, (1 << 20) + 1, 1), "BAD_SHAPE"),   # one past the largest side
+    ((0, 1, (1 << 20) + 1), "BAD_SHAPE"),
     ((0, 6, 6, 0, 20, 3), "BAD_SHAPE"),     # slice length 12 is not a multiple of 8
     ((0, 5, 5, 0, 0, 2), "BAD_SHAPE"),      # 25 % 2
     ((0, 8, 8, 0, 4, 4), "OVERLAP"),        # stride 4 < slice 16
@@ -88,6 +90,12 @@ def test_workspace_bytes_rejects_bad_shapes(lib, item, code):
     rc, _ = ws_bytes(lib, [item])
     assert rc == ERR[code]
     assert lib.muon_last_error() != b""
+
+
+def test_workspace_bytes_accepts_largest_side(lib):
+    for shape in [(0, 1 << 20, 1), (0, 1, 1 << 20)]:
+        rc, b = ws_bytes(lib, [shape])
+        assert rc == 0 and b > 0
 
 
 def test_workspace_bytes_rejects_bad_mode_and_null(lib):

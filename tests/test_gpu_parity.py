@@ -119,6 +119,33 @@ def test_orthogonalize_parity(nsf, torch, mode, ns_steps):
 
 
 @pytest.mark.parametrize("mode", ["f32", "bf16"])
+def test_orthogonalize_maximum_side(nsf, torch, mode):
+    """The largest accepted side, 2^20, as a 1 x 2^20 and a 2^20 x 1 matrix: one
+    64-tile Gram product with 16384 K blocks, 16384 stage-X tiles."""
+    n = 1 << 20
+    say("orthogonalize maximum side", mode, n)
+    descs, uh, oh = _orth_case(nsf, torch, [(1, n), (n, 1)], mode, 5)
+    for d in descs:
+        want = mo.newton_schulz(mat(uh, d).astype(np.float64), 5)
+        err = rel_fro(mat(oh, d), want)
+        say("maximum side", (d.rows, d.cols), err)
+        assert err <= TOL[mode], (d.rows, d.cols, err)
+
+
+def test_orthogonalize_long_float32_contraction(nsf, torch):
+    """float32 products: a 768 x 33000 matrix (256-tile size, but a contraction
+    past 32768) runs on 128-tiles whose Gram product restarts its accumulation
+    chains after 1024 K blocks; O stays within the float32 tolerance."""
+    say("orthogonalize long float32 contraction")
+    descs, uh, oh = _orth_case(nsf, torch, [(768, 33000), (33000, 768)], "f32", 5)
+    for d in descs:
+        want = mo.newton_schulz(mat(uh, d).astype(np.float64), 5)
+        err = rel_fro(mat(oh, d), want)
+        say("long contraction", (d.rows, d.cols), err)
+        assert err <= TOL["f32"], (d.rows, d.cols, err)
+
+
+@pytest.mark.parametrize("mode", ["f32", "bf16"])
 def test_orthogonalize_in_place(nsf, torch, mode):
     shapes = [(100, 37), (37, 100), (256, 256)]
     descs, off = [], 0
