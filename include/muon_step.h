@@ -29,7 +29,11 @@
  * The Frobenius norm is a deterministic float32 reduction.  Newton-Schulz
  * runs either on bfloat16 MFMA with float32 accumulation and float32
  * epilogues, X/A/B stored as bfloat16 (MUON_GEMM_BF16_MFMA), or entirely in
- * float32 on the float32 MFMA (MUON_GEMM_F32).  The first iterate is stored
+ * float32 on the float32 MFMA (MUON_GEMM_F32).  Matrices whose shorter side
+ * is below 160 run in float32 in both modes (with bfloat16 iterates a matrix
+ * with few singular values deviates from the exact iteration by up to ~12%);
+ * in float32 no accumulation chain is longer than 32768 products.  The
+ * first iterate is stored
  * as U itself (rounded to the Newton-Schulz type) and the normalization is
  * applied in float32 inside the first iteration: A0 = inv^2 (U U^T),
  * X1 = inv (a U + B0 U), inv = 1 / (||U||_F + 1e-7) -- the same iterates as

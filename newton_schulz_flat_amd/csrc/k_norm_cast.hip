@@ -102,11 +102,11 @@ __global__ __launch_bounds__(256) void cast_kernel(const MatInfo* __restrict__ m
             const int rr = idx / T, cc = idx % T;
             const int gr = ur0 + rr, gc = uc0 + cc;
             if (gr < mt.R && gc < mt.C)
-                om[int64_t(gr) * mt.C + gc] = mt.scale * rounded(tile[rr][cc], x);
+                om[int64_t(gr) * mt.C + gc] =
+                    mt.scale * (mt.ns_f32 ? tile[rr][cc] : rounded(tile[rr][cc], x));
         }
         return;
     }
-    TX* xm = x + mt.x_off;
     // X0[i][j], i = ti*T + a, j = tj*T + b  (native element tile[a][b] or tile[b][a]);
     // each thread writes 4 consecutive elements of a row
     for (int idx = threadIdx.x; idx < T * T / 4; idx += 256) {
@@ -114,7 +114,11 @@ __global__ __launch_bounds__(256) void cast_kernel(const MatInfo* __restrict__ m
         float v[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) v[t] = tall ? tile[b + t][a] : tile[a][b + t];
-        store_x4(xm + int64_t(ti * T + a) * mt.cp + tj * T + b, v);
+        const int64_t at = int64_t(ti * T + a) * mt.cp + tj * T + b;
+        if (mt.ns_f32)
+            store_x4(reinterpret_cast<float*>(x) + mt.x_off + at, v);
+        else
+            store_x4(x + mt.x_off + at, v);
     }
 }
 
@@ -177,7 +181,13 @@ __global__ __launch_bounds__(256) void front_cast_kernel(const MatInfo* __restri
         }
     };
     float ss = 0.f;
-    TX* xm = x + mt.x_off;
+    // X (NS orientation) at element offset at of this matrix, in its product type
+    auto store_iter4 = [&](int64_t at, const float v[4]) {
+        if (mt.ns_f32)
+            store_x4(reinterpret_cast<float*>(x) + mt.x_off + at, v);
+        else
+            store_x4(x + mt.x_off + at, v);
+    };
     if (!tall) {
         // The iterate has U's own orientation: workgroup t takes the 4096
         // consecutive elements [4096 t, 4096 t + 4096) of the row-major rp x cp
@@ -193,7 +203,7 @@ __global__ __launch_bounds__(256) void front_cast_kernel(const MatInfo* __restri
             front4(i0 + e / mt.cp, e % mt.cp, uv);
 #pragma unroll
             for (int q = 0; q < 4; ++q) ss = ss + uv[q] * uv[q];
-            store_x4(xm + base + o, uv);
+            store_iter4(base + o, uv);
         }
     } else {
         // Tall: workgroup t takes the 64 x 64 tile (ti, tj) of the iterate, read
@@ -232,7 +242,7 @@ __global__ __launch_bounds__(256) void front_cast_kernel(const MatInfo* __restri
             float v[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) v[q] = tile[b + q][a];
-            store_x4(xm + int64_t(ti * T + a) * mt.cp + tj * T + b, v);
+            store_iter4(int64_t(ti * T + a) * mt.cp + tj * T + b, v);
         }
     }
 }

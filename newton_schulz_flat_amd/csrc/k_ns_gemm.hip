@@ -910,7 +910,10 @@ hipError_t launch_class(int tile, int stage, int n_tiles, const NsArgs& a, hipSt
     switch (tile) {
         case 256: return launch_stage<256, BF16>(stage, n_tiles, a, s);
         case 128: return launch_stage<128, BF16>(stage, n_tiles, a, s);
-        default: return launch_stage<64, BF16>(stage, n_tiles, a, s);
+        default:
+            // 64-tiles run in float32 in every mode (kF32NsTile)
+            if constexpr (BF16) return hipErrorInvalidValue;
+            else return launch_stage<64, false>(stage, n_tiles, a, s);
     }
 }
 
@@ -947,8 +950,9 @@ hipError_t launch_newton_schulz(const PlanView& p, void* ws, float* o, const Fus
                 const int count = stage == kStageX ? tc.n_full
                                   : stage == kStageA ? tc.n_sym_a : tc.n_sym_b;
                 a.tiles = stage == kStageX ? tc.full : stage == kStageA ? tc.sym_a : tc.sym_b;
-                const hipError_t e = bf16 ? launch_class<true>(tc.tile, stage, count, a, s)
-                                          : launch_class<false>(tc.tile, stage, count, a, s);
+                const bool cls_bf16 = bf16 && tc.tile != kF32NsTile;
+                const hipError_t e = cls_bf16 ? launch_class<true>(tc.tile, stage, count, a, s)
+                                              : launch_class<false>(tc.tile, stage, count, a, s);
                 if (e != hipSuccess) return e;
             }
         }

@@ -26,6 +26,12 @@ constexpr int64_t kEwChunk = int64_t(kEwThreads) * kEwVec * kEwIters;
 // Square tile of the normalize/cast/orient kernel.
 constexpr int kCastTile = 64;
 
+// GEMM tile of the matrices whose shorter side is below 160.  Their
+// Newton-Schulz products run in float32 in every mode: with bfloat16 iterates
+// a matrix with few singular values keeps none of the averaging that holds
+// large matrices to ~1e-2, and deviates from the exact iteration by up to ~12%.
+constexpr int kF32NsTile = 64;
+
 // Alignment of every workspace region, in bytes.
 constexpr size_t kWsAlign = 256;
 
@@ -62,7 +68,8 @@ struct alignas(16) MatInfo {
     int32_t cast_begin, n_cast;     // normalize/cast tiles
     float scale;        // (float) sqrt(max(1, R/C))
     int32_t group;      // optimizer group (muon_step_grouped), else 0
-    int32_t pad_[2];
+    int32_t ns_f32;     // products, X, A and B in float32 (x_off, g_off count floats)
+    int32_t pad_;
 };
 static_assert(sizeof(MatInfo) == 128, "MatInfo layout");
 

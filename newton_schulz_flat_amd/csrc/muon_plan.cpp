@@ -58,11 +58,12 @@ struct Geometry {
 
 Geometry build_geometry(const muon_matrix_desc_t* d, int64_t n, int gemm_mode) {
     Geometry g;
-    const size_t es = gemm_mode == MUON_GEMM_F32 ? 4 : 2;
     g.mats.resize(size_t(n));
     g.chunk_prefix.assign(size_t(n) + 1, 0);
     g.cast_prefix.assign(size_t(n) + 1, 0);
-    int64_t x_elems = 0, g_elems = 0, chunks = 0, casts = 0;
+    // X, A and B regions in bytes; each matrix's offsets count elements of its
+    // own product type (2 or 4 bytes)
+    int64_t x_bytes = 0, g_bytes = 0, chunks = 0, casts = 0;
     for (int64_t i = 0; i < n; ++i) {
         MatInfo& m = g.mats[size_t(i)];
         std::memset(&m, 0, sizeof(m));
@@ -81,11 +82,13 @@ Geometry build_geometry(const muon_matrix_desc_t* d, int64_t n, int gemm_mode) {
         m.cp = int32_t(round_up(m.c, m.tile));
         m.scale = float(std::sqrt(std::max(1.0, double(m.R) / double(m.C))));
         m.group = d[i].group;
+        m.ns_f32 = gemm_mode == MUON_GEMM_F32 || m.tile == kF32NsTile;
+        const int64_t es = m.ns_f32 ? 4 : 2;
         // Every region start stays 256-byte aligned: rp and cp are multiples of 64.
-        m.x_off = x_elems;
-        x_elems += int64_t(m.rp) * m.cp;
-        m.g_off = g_elems;
-        g_elems += int64_t(m.rp) * m.rp;
+        m.x_off = x_bytes / es;
+        x_bytes += int64_t(m.rp) * m.cp * es;
+        m.g_off = g_bytes / es;
+        g_bytes += int64_t(m.rp) * m.rp * es;
         m.n_chunks = int32_t((m.numel + kEwChunk - 1) / kEwChunk);
         m.chunk_begin = int32_t(chunks);
         chunks += m.n_chunks;
@@ -103,13 +106,13 @@ Geometry build_geometry(const muon_matrix_desc_t* d, int64_t n, int gemm_mode) {
     // The second X region starts 64 KiB past an alignment boundary so that the
     // two iterates never alias at a power-of-two distance.
     w.x[0] = at;
-    at = align_up(at + size_t(x_elems) * es, kWsAlign) + (size_t(1) << 16);
+    at = align_up(at + size_t(x_bytes), kWsAlign) + (size_t(1) << 16);
     w.x[1] = at;
-    at = align_up(at + size_t(x_elems) * es, kWsAlign);
+    at = align_up(at + size_t(x_bytes), kWsAlign);
     w.a = at;
-    at = align_up(at + size_t(g_elems) * es, kWsAlign);
+    at = align_up(at + size_t(g_bytes), kWsAlign);
     w.b = at;
-    at = align_up(at + size_t(g_elems) * es, kWsAlign);
+    at = align_up(at + size_t(g_bytes), kWsAlign);
     // partial sums: one per elementwise chunk or one per cast tile
     w.partial = at;
     at = align_up(at + size_t(std::max<int64_t>(chunks, casts)) * 4, kWsAlign);

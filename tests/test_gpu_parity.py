@@ -132,6 +132,24 @@ def test_orthogonalize_maximum_side(nsf, torch, mode):
         assert err <= TOL[mode], (d.rows, d.cols, err)
 
 
+@pytest.mark.parametrize("mode", ["f32", "bf16"])
+def test_many_tiny_matrices(nsf, torch, mode):
+    """3000 matrices with sides 1..24 in one call: the matrix search over the
+    prefix tables and the grouped tile tables at large matrix counts."""
+    rng = np.random.default_rng(31)
+    shapes = [tuple(int(v) for v in rng.integers(1, 25, size=2)) for _ in range(3000)]
+    say("many tiny matrices", mode, len(shapes))
+    descs, uh, oh = _orth_case(nsf, torch, shapes, mode, 5, seed=7)
+    worst = 0.0
+    for d in descs:
+        want = mo.newton_schulz(mat(uh, d).astype(np.float64), 5)
+        worst = max(worst, rel_fro(mat(oh, d), want))
+    say("many tiny worst rel err", mode, worst)
+    assert worst <= TOL[mode]
+    cov = covered_mask(uh.size, descs, "state")
+    assert np.all(oh[~cov] == 3.0)
+
+
 def test_orthogonalize_long_float32_contraction(nsf, torch):
     """float32 products: a 768 x 33000 matrix (256-tile size, but a contraction
     past 32768) runs on 128-tiles whose Gram product restarts its accumulation
