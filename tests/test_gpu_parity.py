@@ -150,6 +150,54 @@ def test_many_tiny_matrices(nsf, torch, mode):
     assert np.all(oh[~cov] == 3.0)
 
 
+@pytest.mark.parametrize("rank", [1, 8])
+def test_rank_deficient_float32(nsf, torch, rank):
+    """Rank-deficient inputs U = P Q (P 1024 x rank, Q rank x 1024; 256 x rank,
+    rank x 512), float32 mode.  The exact O lives in U's column and row spaces;
+    what the iteration does with U's null space is not unique in finite
+    precision: each step multiplies a perturbation there by f'(0) = a, so
+    rounding noise of relative size e (float32 products over K terms: about
+    sqrt(K) 2^-24) grows to about a^5 e.  Checked: the projection of O onto U's
+    column and row spaces against the fp64 oracle within the float32 tolerance,
+    and the rest of O within a^5 sqrt(K) 2^-24 of ||O||."""
+    say("rank deficient float32", rank)
+    shapes = [(1024, 1024), (256, 512)]
+    descs, off = [], 0
+    for r, c in shapes:
+        descs.append(wlm.Desc(off, r, c, off))
+        off += (r * c + 63) // 64 * 64 + 64
+    g = torch.Generator("cuda").manual_seed(300 + rank)
+    u = torch.zeros(off, device="cuda")
+    for d in descs:
+        p = torch.randn(d.rows, rank, device="cuda", generator=g)
+        q = torch.randn(rank, d.cols, device="cuda", generator=g)
+        u[d.offset:d.offset + d.rows * d.cols] = (p @ q).reshape(-1) * 1e-3
+    o = torch.zeros_like(u)
+    nsf.muon_orthogonalize(u, o, descs, mode="f32")
+    gpu_sync(torch)
+    uh, oh = host(u), host(o)
+    a5 = 3.4445 ** 5
+    for d in descs:
+        u64 = mat(uh, d).astype(np.float64)
+        want = mo.newton_schulz(u64, 5)
+        pl, sv, qr = np.linalg.svd(u64, full_matrices=False)
+        # the float32 input itself carries rounding noise (~1e-7 relative) in
+        # the null space: count only the singular values above it
+        k = int(np.sum(sv > sv[0] * 1e-5))
+        pk, qk = pl[:, :k], qr[:k].T
+        got = mat(oh, d).astype(np.float64)
+        def project(m):
+            return pk @ (pk.T @ m @ qk) @ qk.T
+        in_range = project(got)
+        err_range = rel_fro(in_range, project(want))
+        rest = np.linalg.norm(got - in_range) / np.linalg.norm(want)
+        bound = a5 * np.sqrt(max(d.rows, d.cols)) * 2.0 ** -24  # K of the Gram product
+        say("rank", rank, (d.rows, d.cols), "k", k, "range", err_range, "rest", rest, "bound", bound)
+        assert k == rank
+        assert err_range <= TOL["f32"], (rank, d.rows, d.cols, err_range)
+        assert rest <= bound, (rank, d.rows, d.cols, rest, bound)
+
+
 def test_orthogonalize_long_float32_contraction(nsf, torch):
     """float32 products: a 768 x 33000 matrix (256-tile size, but a contraction
     past 32768) runs on 128-tiles whose Gram product restarts its accumulation
