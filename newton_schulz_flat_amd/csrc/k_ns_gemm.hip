@@ -34,6 +34,7 @@
 // fragment reads of 8 consecutive rows hit distinct banks.  One grouped launch
 // per stage and tile size covers every matrix, driven by a tile table.
 #include <type_traits>
+#include <utility>
 
 #include "k_common.h"
 
@@ -245,6 +246,80 @@ __device__ __forceinline__ void apply_span(TW* __restrict__ params, uint16_t* co
             }
         }
     }
+}
+
+// One staged 32-row band of O (kT 4-element chunks per lane, chunk t of lane l
+// at staged row (64 t + l) / cpr, column 4 ((64 t + l) % cpr), O element
+// (a0 + row, b0 + column)) applied to the weights: every aligned 4-element
+// group's weights are loaded before any is updated, so that one wave has all
+// of its band's loads in flight at once; ragged groups take apply_span.
+template <int kT, typename TW>
+__device__ __forceinline__ void apply_band(TW* __restrict__ params, uint16_t* copy, const MatInfo& mt,
+                                           const float* wl, int pitch, int cpr, int a0, int b0,
+                                           int rows_o, int cols_o, float decay, float lr, int lane) {
+#pragma clang fp contract(off)
+    const int64_t slice = mt.slice_len;
+    const bool sharded = slice != mt.numel;
+    // two halves of kT / 2 chunks: loads of a half, then its updates
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        constexpr int kH = kT / 2;
+        int64_t dst[kH];
+        float w[kH][4];
+#pragma unroll
+        for (int t = 0; t < kH; ++t) {
+            const int ch = (h * kH + t) * 64 + lane, lrow = ch / cpr, lc = (ch % cpr) * 4;
+            const int a = a0 + lrow, b = b0 + lc;
+            const int64_t e = int64_t(a) * cols_o + b;
+            dst[t] = -1;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) w[t][u] = 0.f;
+            if (a < rows_o && b + 3 < cols_o && (e & 3) == 0) {
+                // sharded slices are multiples of 8 long: an aligned group of 4 never straddles two
+                int64_t d = mt.poff + e;
+                if (sharded) {
+                    const int64_t k = e / slice;
+                    d = mt.poff + k * mt.pstride + (e - k * slice);
+                }
+                dst[t] = d;
+                load_w4(params + d, w[t]);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < kH; ++t) {
+            const int ch = (h * kH + t) * 64 + lane, lrow = ch / cpr, lc = (ch % cpr) * 4;
+            const int a = a0 + lrow, b = b0 + lc;
+            if (a < rows_o && b < cols_o) {
+                const float4 q = *reinterpret_cast<const float4*>(wl + lrow * pitch + lc);
+                const float ov[4] = {q.x, q.y, q.z, q.w};
+                if (dst[t] >= 0) {
+                    float r[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const float w1 = w[t][u] * decay;
+                        const float up = lr * ov[u];
+                        r[u] = w1 - up;
+                    }
+                    store_w4(params + dst[t], r);
+                    if (copy != nullptr) store_w4(copy + dst[t], r);
+                } else {
+                    const int cnt = b + 3 < cols_o ? 4 : cols_o - b;
+                    apply_span(params, copy, mt, int64_t(a) * cols_o + b, cnt, ov, decay, lr);
+                }
+            }
+        }
+    }
+}
+
+// f(std::integral_constant<int, 0>{}), ..., f(std::integral_constant<int, N - 1>{}):
+// a loop whose index is a compile-time constant in every instance.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // Two transposing LDS reads at p and p + second, as one 8-element MFMA operand.
@@ -808,72 +883,90 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
         static_assert(kRegionL * G::kWaves <= 2 * kBuf, "epilogue staging exceeds LDS");
         float* wl = reinterpret_cast<float*>(lds + wave * kRegionL);
         const int r0w = ti * TILE + wm * G::kWm, c0w = tj * TILE + wn * kWn;
-#pragma unroll
-        for (int i = 0; i < kMi; ++i) {
+        constexpr int kT = 32 * kWn / 4 / 64;  // 4-element chunks per lane and band
+        // the band loop once per output kind (weights of type TW, or O), so that
+        // each instance unrolls fully and the accumulators keep static indices
+        auto bands = [&](auto* params, uint16_t* copy, auto fuse_tag) {
+            constexpr bool kFuse = decltype(fuse_tag)::value;
+            // X rows of band 0; band i + 1 is loaded while band i is written out
             Raw4<TE> raw[kNj][4];
 #pragma unroll
             for (int j = 0; j < kNj; ++j)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) raw[j][g] = load_raw4(x_row(i, j, g));
-            __builtin_amdgcn_sched_barrier(0);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // previous band read back
+                for (int g = 0; g < 4; ++g) raw[j][g] = load_raw4(x_row(0, j, g));
+            static_for<kMi>([&](auto i_tag) {
+                constexpr int i = decltype(i_tag)::value;
+                __builtin_amdgcn_sched_barrier(0);
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // previous band read back
 #pragma unroll
-            for (int j = 0; j < kNj; ++j) {
+                for (int j = 0; j < kNj; ++j) {
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    float v[4], xv[4], w[4];
-                    decode4(raw[j][g], xv);  // row layout
-                    if (tall) {
-                        // O[gj][gi + t] = X[gi + t][gj]: the column layout, 4 consecutive O elements
-                        float xcol[4];
-                        quad_transpose(xv, xcol, s4);
+                    for (int g = 0; g < 4; ++g) {
+                        float v[4], xv[4], w[4];
+                        decode4(raw[j][g], xv);  // row layout
+                        if (tall) {
+                            // O[gj][gi + t] = X[gi + t][gj]: the column layout, 4 consecutive O elements
+                            float xcol[4];
+                            quad_transpose(xv, xcol, s4);
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) v[t] = sc * (xs * (ca * xcol[t] + acc[i][j][g * 4 + t]));
-                        *reinterpret_cast<float4*>(wl + (j * 32 + lr) * kPT + g * 8 + (lane >> 5) * 4) =
-                            make_float4(v[0], v[1], v[2], v[3]);
-                    } else {
-                        // O[gi + s][gj - s + t]: the row layout after the quad exchange
+                            for (int t = 0; t < 4; ++t)
+                                v[t] = sc * (xs * (ca * xcol[t] + acc[i][j][g * 4 + t]));
+                            *reinterpret_cast<float4*>(wl + (j * 32 + lr) * kPT + g * 8 + (lane >> 5) * 4) =
+                                make_float4(v[0], v[1], v[2], v[3]);
+                        } else {
+                            // O[gi + s][gj - s + t]: the row layout after the quad exchange
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) v[t] = acc[i][j][g * 4 + t];
-                        quad_transpose(v, w, s4);
+                            for (int t = 0; t < 4; ++t) v[t] = acc[i][j][g * 4 + t];
+                            quad_transpose(v, w, s4);
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) w[t] = sc * (xs * (ca * xv[t] + w[t]));
-                        *reinterpret_cast<float4*>(wl + (g * 8 + (lane >> 5) * 4 + s4) * kPN + j * 32 + lr - s4) =
-                            make_float4(w[0], w[1], w[2], w[3]);
+                            for (int t = 0; t < 4; ++t) w[t] = sc * (xs * (ca * xv[t] + w[t]));
+                            *reinterpret_cast<float4*>(wl + (g * 8 + (lane >> 5) * 4 + s4) * kPN + j * 32 +
+                                                       lr - s4) = make_float4(w[0], w[1], w[2], w[3]);
+                        }
                     }
                 }
-            }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            // the band is 32 x kWn (wide) or kWn x 32 (tall) O elements; 4 per lane per pass
-            const int cpr = tall ? 8 : kWn / 4;  // 4-element chunks per staged row
-            const int pitch = tall ? kPT : kPN;
-            const int a0 = tall ? c0w : r0w + i * 32, b0 = tall ? r0w + i * 32 : c0w;
-#pragma unroll 2
-            for (int t = 0; t < 32 * kWn / 4 / 64; ++t) {
-                const int ch = t * 64 + lane, lrow = ch / cpr, lc = (ch % cpr) * 4;
-                const int a = a0 + lrow, b = b0 + lc;
-                if (a < rows_o && b < cols_o) {
-                    const float4 q = *reinterpret_cast<const float4*>(wl + lrow * pitch + lc);
-                    const float ov[4] = {q.x, q.y, q.z, q.w};
-                    const int cnt = b + 3 < cols_o ? 4 : cols_o - b;
-                    const int64_t e = int64_t(a) * cols_o + b;
-                    if (args.fuse) {
-                        if (args.param_bf16)
-                            apply_span(static_cast<uint16_t*>(args.params), nullptr, mt, e, cnt, ov, hv.decay,
-                                       hv.lr);
-                        else
-                            apply_span(static_cast<float*>(args.params), args.model_copy, mt, e, cnt, ov,
-                                       hv.decay, hv.lr);
-                    } else if (cnt == 4 && (e & 3) == 0) {
-                        store4(om + e, ov);
-                    } else {
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                if constexpr (i + 1 < kMi) {
 #pragma unroll
-                        for (int u = 0; u < 4; ++u)
-                            if (u < cnt) om[e + u] = ov[u];
+                    for (int j = 0; j < kNj; ++j)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) raw[j][g] = load_raw4(x_row(i + 1, j, g));
+                }
+                // the band is 32 x kWn (wide) or kWn x 32 (tall) O elements; 4 per lane per pass
+                const int cpr = tall ? 8 : kWn / 4;  // 4-element chunks per staged row
+                const int pitch = tall ? kPT : kPN;
+                const int a0 = tall ? c0w : r0w + i * 32, b0 = tall ? r0w + i * 32 : c0w;
+                if constexpr (kFuse) {
+                    apply_band<kT>(params, copy, mt, wl, pitch, cpr, a0, b0, rows_o, cols_o, hv.decay,
+                                   hv.lr, lane);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < kT; ++t) {
+                        const int ch = t * 64 + lane, lrow = ch / cpr, lc = (ch % cpr) * 4;
+                        const int a = a0 + lrow, b = b0 + lc;
+                        if (a < rows_o && b < cols_o) {
+                            const float4 q = *reinterpret_cast<const float4*>(wl + lrow * pitch + lc);
+                            const float ov[4] = {q.x, q.y, q.z, q.w};
+                            const int cnt = b + 3 < cols_o ? 4 : cols_o - b;
+                            const int64_t e = int64_t(a) * cols_o + b;
+                            if (cnt == 4 && (e & 3) == 0) {
+                                store4(om + e, ov);
+                            } else {
+#pragma unroll
+                                for (int u = 0; u < 4; ++u)
+                                    if (u < cnt) om[e + u] = ov[u];
+                            }
+                        }
                     }
                 }
-            }
-        }
+            });
+        };
+        if (!args.fuse)
+            bands(static_cast<float*>(nullptr), nullptr, std::false_type{});
+        else if (args.param_bf16)
+            bands(static_cast<uint16_t*>(args.params), nullptr, std::true_type{});
+        else
+            bands(static_cast<float*>(args.params), args.model_copy, std::true_type{});
     }
 }
 
