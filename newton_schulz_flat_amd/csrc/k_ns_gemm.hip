@@ -253,27 +253,27 @@ __device__ __forceinline__ void apply_span(TW* __restrict__ params, uint16_t* co
 // (a0 + row, b0 + column)) applied to the weights: every aligned 4-element
 // group's weights are loaded before any is updated, so that one wave has all
 // of its band's loads in flight at once; ragged groups take apply_span.
-template <int kT, typename TW>
+template <int kT, int kParts, typename TW>
 __device__ __forceinline__ void apply_band(TW* __restrict__ params, uint16_t* copy, const MatInfo& mt,
                                            const float* wl, int pitch, int cpr, int a0, int b0,
                                            int rows_o, int cols_o, float decay, float lr, int lane) {
 #pragma clang fp contract(off)
     const int64_t slice = mt.slice_len;
     const bool sharded = slice != mt.numel;
-    // two halves of kT / 2 chunks: loads of a half, then its updates
+    // the loads of a part (the whole band, or a half where registers are short),
+    // then its updates
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        constexpr int kH = kT / 2;
+    for (int h = 0; h < kParts; ++h) {
+        constexpr int kH = kT / kParts;
         int64_t dst[kH];
-        float w[kH][4];
+        Raw4<TW> w[kH];  // undecoded
 #pragma unroll
         for (int t = 0; t < kH; ++t) {
             const int ch = (h * kH + t) * 64 + lane, lrow = ch / cpr, lc = (ch % cpr) * 4;
             const int a = a0 + lrow, b = b0 + lc;
             const int64_t e = int64_t(a) * cols_o + b;
             dst[t] = -1;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) w[t][u] = 0.f;
+            w[t] = Raw4<TW>{};
             if (a < rows_o && b + 3 < cols_o && (e & 3) == 0) {
                 // sharded slices are multiples of 8 long: an aligned group of 4 never straddles two
                 int64_t d = mt.poff + e;
@@ -282,7 +282,7 @@ __device__ __forceinline__ void apply_band(TW* __restrict__ params, uint16_t* co
                     d = mt.poff + k * mt.pstride + (e - k * slice);
                 }
                 dst[t] = d;
-                load_w4(params + d, w[t]);
+                w[t] = load_raw4(params + d);
             }
         }
 #pragma unroll
@@ -293,10 +293,11 @@ __device__ __forceinline__ void apply_band(TW* __restrict__ params, uint16_t* co
                 const float4 q = *reinterpret_cast<const float4*>(wl + lrow * pitch + lc);
                 const float ov[4] = {q.x, q.y, q.z, q.w};
                 if (dst[t] >= 0) {
-                    float r[4];
+                    float wv[4], r[4];
+                    decode4(w[t], wv);
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
-                        const float w1 = w[t][u] * decay;
+                        const float w1 = wv[u] * decay;
                         const float up = lr * ov[u];
                         r[u] = w1 - up;
                     }
@@ -937,8 +938,11 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                 const int pitch = tall ? kPT : kPN;
                 const int a0 = tall ? c0w : r0w + i * 32, b0 = tall ? r0w + i * 32 : c0w;
                 if constexpr (kFuse) {
-                    apply_band<kT>(params, copy, mt, wl, pitch, cpr, a0, b0, rows_o, cols_o, hv.decay,
-                                   hv.lr, lane);
+                    // whole bands of bfloat16 weights in the bfloat16 kernels, else halves
+                    constexpr int kParts =
+                        (BF16 && sizeof(std::remove_pointer_t<decltype(params)>) == 2) ? 1 : 2;
+                    apply_band<kT, kParts>(params, copy, mt, wl, pitch, cpr, a0, b0, rows_o, cols_o,
+                                           hv.decay, hv.lr, lane);
                 } else {
 #pragma unroll
                     for (int t = 0; t < kT; ++t) {
