@@ -142,41 +142,58 @@ __global__ __launch_bounds__(256) void front_cast_kernel(const MatInfo* __restri
     const HyperVals hv = hyper_for(h, mt);
     const float beta = hv.beta;
     const int nesterov = hv.nesterov;
-    // U at 4 consecutive elements of U's row gr from column gc (zero outside
-    // R x C); with kStep, M is updated there.
-    auto front4 = [&](int gr, int gc, float uv[4]) {
-        uv[0] = uv[1] = uv[2] = uv[3] = 0.f;
+    // Each thread first loads all of its G and M (or U) groups and only then
+    // stores: vector memory counters complete in issue order and count stores,
+    // so a load issued after a store could not be waited for without waiting
+    // for the store.
+    // G and M (or U, in gv) at 4 consecutive elements of U's row gr from column
+    // gc; zero outside R x C.
+    auto load4 = [&](int gr, int gc, float gv[4], float mv[4]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) gv[q] = mv[q] = 0.f;
         if (gr >= mt.R || gc >= mt.C) return;
         const int64_t e = mt.off + int64_t(gr) * mt.C + gc;
         if (vec && gc + 3 < mt.C) {
+            const float4 a4 = load4_stream((kStep ? g : u_in) + e);
+            gv[0] = a4.x, gv[1] = a4.y, gv[2] = a4.z, gv[3] = a4.w;
             if (kStep) {
-                const float4 gv = load4_stream(g + e);
-                const float4 mv = load4_stream(m + e);
-                const float g4[4] = {gv.x, gv.y, gv.z, gv.w};
-                const float m4[4] = {mv.x, mv.y, mv.z, mv.w};
-                float m1[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    m1[q] = beta * m4[q] + g4[q];
-                    uv[q] = nesterov ? beta * m1[q] + g4[q] : m1[q];
-                }
-                store4_stream(m + e, make_float4(m1[0], m1[1], m1[2], m1[3]));
-            } else {
-                const float4 q4 = load4_stream(u_in + e);
-                uv[0] = q4.x, uv[1] = q4.y, uv[2] = q4.z, uv[3] = q4.w;
+                const float4 b4 = load4_stream(m + e);
+                mv[0] = b4.x, mv[1] = b4.y, mv[2] = b4.z, mv[3] = b4.w;
             }
         } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 if (gc + q < mt.C) {
-                    if (kStep) {
-                        const float m1 = beta * m[e + q] + g[e + q];
-                        m[e + q] = m1;
-                        uv[q] = nesterov ? beta * m1 + g[e + q] : m1;
-                    } else {
-                        uv[q] = u_in[e + q];
-                    }
+                    gv[q] = (kStep ? g : u_in)[e + q];
+                    if (kStep) mv[q] = m[e + q];
                 }
+            }
+        }
+    };
+    // U from the loaded values; with kStep, M <- fl(fl(beta M) + G) is stored
+    auto update4 = [&](int gr, int gc, const float gv[4], const float mv[4], float uv[4]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) uv[q] = 0.f;
+        if (gr >= mt.R || gc >= mt.C) return;
+        if (!kStep) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) uv[q] = gv[q];
+            return;
+        }
+        const int64_t e = mt.off + int64_t(gr) * mt.C + gc;
+        float m1[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            m1[q] = beta * mv[q] + gv[q];
+            uv[q] = nesterov ? beta * m1[q] + gv[q] : m1[q];
+        }
+        if (vec && gc + 3 < mt.C) {
+            store4_stream(m + e, make_float4(m1[0], m1[1], m1[2], m1[3]));
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (gc + q < mt.C) m[e + q] = m1[q];
+                else uv[q] = 0.f;
             }
         }
     };
@@ -195,15 +212,21 @@ __global__ __launch_bounds__(256) void front_cast_kernel(const MatInfo* __restri
         // it * 256 + tid, so that G, M and X stream along rows.
         const int64_t base = int64_t(t) * (T * T);
         const int i0 = int(base / mt.cp), j0 = int(base % mt.cp);
+        int gr[kIters], gc[kIters];
+        float gv[kIters][4], mv[kIters][4];
 #pragma unroll
         for (int it = 0; it < kIters; ++it) {
-            const int o = (it * 256 + int(threadIdx.x)) * 4;
-            const int e = j0 + o;
+            const int e = j0 + (it * 256 + int(threadIdx.x)) * 4;
+            gr[it] = i0 + e / mt.cp, gc[it] = e % mt.cp;
+            load4(gr[it], gc[it], gv[it], mv[it]);
+        }
+#pragma unroll
+        for (int it = 0; it < kIters; ++it) {
             float uv[4];
-            front4(i0 + e / mt.cp, e % mt.cp, uv);
+            update4(gr[it], gc[it], gv[it], mv[it], uv);
 #pragma unroll
             for (int q = 0; q < 4; ++q) ss = ss + uv[q] * uv[q];
-            store_iter4(base + o, uv);
+            store_iter4(base + (it * 256 + int(threadIdx.x)) * 4, uv);
         }
     } else {
         // Tall: workgroup t takes the 64 x 64 tile (ti, tj) of the iterate, read
@@ -214,12 +237,18 @@ __global__ __launch_bounds__(256) void front_cast_kernel(const MatInfo* __restri
         const int nti = mt.rp / T;
         const int tj = t / nti, ti = t % nti;
         const int ur0 = tj * T, uc0 = ti * T;  // tile origin in U's (R x C) coordinates
+        float gv[kIters][4], mv[kIters][4];
+#pragma unroll
+        for (int it = 0; it < kIters; ++it) {
+            const int seg = it * 256 + int(threadIdx.x);
+            load4(ur0 + (seg >> 4), uc0 + (seg & 15) * 4, gv[it], mv[it]);
+        }
 #pragma unroll
         for (int it = 0; it < kIters; ++it) {
             const int seg = it * 256 + int(threadIdx.x);
             const int rr = seg >> 4, c4 = (seg & 15) * 4;
             float uv[4];
-            front4(ur0 + rr, uc0 + c4, uv);
+            update4(ur0 + rr, uc0 + c4, gv[it], mv[it], uv);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 tile[rr][c4 + q] = uv[q];
