@@ -12,27 +12,29 @@
 // layout wants each lane to hold consecutive K values of one operand row (8
 // for bf16), so operand tiles are staged in LDS as rows along K.  For P and
 // for the symmetric stages those are rows of the stored matrices; stage X's
-// Q = X^T is never stored: its loader reads blocks of consecutive rows of X
-// (a few K values by 16 bytes of columns) and transposes them in registers on
-// their way into LDS.
+// Q = X^T is never stored: bfloat16 stage X stages K rows of X as they are and
+// its fragment reads transpose them (ds_read_b64_tr_b16); float32 stage X
+// transposes blocks of X in registers on their way into LDS.
 //
 // Symmetric stages compute only tiles with ti <= tj and mirror each
 // off-diagonal tile into (tj, ti).  The axpys b A + c (.) and a X + (.) run in
-// float32 in the epilogues; the stage-B epilogue reads A along a column
-// (A is symmetric), whose 4 consecutive elements match the 4 consecutive
-// output rows each lane holds; the stage-X epilogue first exchanges its
-// results across lane quads into row order and then reads X along rows.
+// float32 in the epilogues: the bfloat16 epilogues bring their operand into
+// the accumulator layout, and their results into row order, through LDS
+// transposing reads; the float32 ones exchange values across lane quads.
 // X ping-pongs between two buffers (workgroups of stage X still read the
 // current X while others write the next one); on the last iteration stage X
-// writes O = fl(s * X) in the matrix's original orientation instead.
+// writes O = fl(s * X) in the matrix's original orientation instead, or
+// applies the decay and update to the weights at once.  Iteration 0 scales its
+// products by the matrix's 1 / ||U|| (the first iterate is U itself).
 //
 // Workgroup: 4 waves in a 2 x 2 grid over a TILE x TILE output tile (8 waves,
 // 2 x 4, for the 256 x 256 bf16 tile); each wave owns its block of outputs as
-// 32 x 32 MFMA fragments.  K is
-// consumed in blocks of 128 bytes per row (64 bf16 / 32 float32), staged
-// through double-buffered LDS with rows padded to 144 bytes so that the 16-byte
-// fragment reads of 8 consecutive rows hit distinct banks.  One grouped launch
-// per stage and tile size covers every matrix, driven by a tile table.
+// 32 x 32 MFMA fragments.  K is consumed in blocks of 128 bytes per row (64
+// bf16 / 32 float32), staged through double-buffered LDS with rows padded to
+// 144 bytes so that the 16-byte fragment reads of 8 consecutive rows hit
+// distinct banks.  One grouped launch per stage and tile size covers every
+// matrix, driven by a tile table.  The 64-tiles run in float32 in every mode;
+// float32 64/128-tiles restart their accumulation chains every 1024 K blocks.
 #include <type_traits>
 #include <utility>
 

@@ -193,11 +193,12 @@ hipError_t launch_sumsq(const PlanView& p, const float* u, float* partial, hipSt
 // or per 64 x 64 cast tile (per_tile).
 hipError_t launch_norm(const PlanView& p, const float* partial, float* inv, bool per_tile,
                        hipStream_t s);
-// One pass per 64 x 64 tile: with u == nullptr, momentum and input from grads
-// and momentum (momentum updated); else U is read.  Writes U, rounded to the NS
-// type but not normalized, as the first iterate in NS orientation (zero
-// padding) and the per-tile sums of squares of U.  The Newton-Schulz iteration
-// 0 then applies 1 / ||U|| (launch_newton_schulz with the norm folded).
+// One pass over the first iterate, one workgroup per 4096 of its elements:
+// with u == nullptr, momentum and input from grads and momentum (momentum
+// updated); else U is read.  Writes U, rounded to the matrix's product type but
+// not normalized, as the first iterate in NS orientation (zero padding) and
+// one sum of squares of U per workgroup.  The Newton-Schulz iteration 0 then
+// applies 1 / ||U|| (launch_newton_schulz with the norm folded).
 hipError_t launch_front_cast(const PlanView& p, const float* grads, float* momentum,
                              const float* u, const Hyper& h, void* ws, float* partial,
                              hipStream_t s);
