@@ -208,6 +208,17 @@ __device__ __forceinline__ float load_w1(const float* p) { return *p; }
 __device__ __forceinline__ float load_w1(const uint16_t* p) { return __uint_as_float(uint32_t(*p) << 16); }
 __device__ __forceinline__ void store_w1(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_w1(uint16_t* p, float v) { *p = bf16_rne(v); }
+// The same four elements where they are not 4-aligned (O rows whose length
+// is not a multiple of 4): element accesses.
+__device__ __forceinline__ Raw4<float> load_raw4_u(const float* p) { return {make_float4(p[0], p[1], p[2], p[3])}; }
+__device__ __forceinline__ Raw4<uint16_t> load_raw4_u(const uint16_t* p) {
+    return {make_uint2(uint32_t(p[0]) | (uint32_t(p[1]) << 16), uint32_t(p[2]) | (uint32_t(p[3]) << 16))};
+}
+template <typename TW>
+__device__ __forceinline__ void store_w4_u(TW* p, const float r[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) store_w1(p + u, r[u]);
+}
 
 template <typename TW>
 __device__ __forceinline__ void apply_span(TW* __restrict__ params, uint16_t* copy, const MatInfo& mt,
@@ -252,10 +263,14 @@ __device__ __forceinline__ void apply_span(TW* __restrict__ params, uint16_t* co
 
 // One staged 32-row band of O (kT 4-element chunks per lane, chunk t of lane l
 // at staged row (64 t + l) / cpr, column 4 ((64 t + l) % cpr), O element
-// (a0 + row, b0 + column)) applied to the weights: every aligned 4-element
-// group's weights are loaded before any is updated, so that one wave has all
-// of its band's loads in flight at once; ragged groups take apply_span.
-template <int kT, int kParts, typename TW>
+// (a0 + row, b0 + column)) applied to the weights: the weights of every
+// aligned 4-element group are loaded before any is updated, so that one wave
+// has all of its band's loads in flight at once; ragged groups take
+// apply_span.  kU (O rows not a multiple of 4 long, unsharded matrix): every
+// complete group is loaded and stored element by element, its loads still
+// issued with the band's -- apply_span would wait for a store round trip per
+// element, since a load issued after a store completes only after it.
+template <int kT, int kParts, bool kU, typename TW>
 __device__ __forceinline__ void apply_band(TW* __restrict__ params, uint16_t* copy, const MatInfo& mt,
                                            const float* wl, int pitch, int cpr, int a0, int b0,
                                            int rows_o, int cols_o, float decay, float lr, int lane) {
@@ -276,7 +291,12 @@ __device__ __forceinline__ void apply_band(TW* __restrict__ params, uint16_t* co
             const int64_t e = int64_t(a) * cols_o + b;
             dst[t] = -1;
             w[t] = Raw4<TW>{};
-            if (a < rows_o && b + 3 < cols_o && (e & 3) == 0) {
+            if constexpr (kU) {
+                if (a < rows_o && b + 3 < cols_o) {
+                    dst[t] = mt.poff + e;
+                    w[t] = load_raw4_u(params + dst[t]);
+                }
+            } else if (a < rows_o && b + 3 < cols_o && (e & 3) == 0) {
                 // sharded slices are multiples of 8 long: an aligned group of 4 never straddles two
                 int64_t d = mt.poff + e;
                 if (sharded) {
@@ -303,8 +323,13 @@ __device__ __forceinline__ void apply_band(TW* __restrict__ params, uint16_t* co
                         const float up = lr * ov[u];
                         r[u] = w1 - up;
                     }
-                    store_w4(params + dst[t], r);
-                    if (copy != nullptr) store_w4(copy + dst[t], r);
+                    if constexpr (kU) {
+                        store_w4_u(params + dst[t], r);
+                        if (copy != nullptr) store_w4_u(copy + dst[t], r);
+                    } else {
+                        store_w4(params + dst[t], r);
+                        if (copy != nullptr) store_w4(copy + dst[t], r);
+                    }
                 } else {
                     const int cnt = b + 3 < cols_o ? 4 : cols_o - b;
                     apply_span(params, copy, mt, int64_t(a) * cols_o + b, cnt, ov, decay, lr);
@@ -889,8 +914,9 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
         constexpr int kT = 32 * kWn / 4 / 64;  // 4-element chunks per lane and band
         // the band loop once per output kind (weights of type TW, or O), so that
         // each instance unrolls fully and the accumulators keep static indices
-        auto bands = [&](auto* params, uint16_t* copy, auto fuse_tag) {
+        auto bands = [&](auto* params, uint16_t* copy, auto fuse_tag, auto u_tag) {
             constexpr bool kFuse = decltype(fuse_tag)::value;
+            constexpr bool kU = decltype(u_tag)::value;
             // X rows of band 0; band i + 1 is loaded while band i is written out
             Raw4<TE> raw[kNj][4];
 #pragma unroll
@@ -943,8 +969,8 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                     // whole bands of bfloat16 weights in the bfloat16 kernels, else halves
                     constexpr int kParts =
                         (BF16 && sizeof(std::remove_pointer_t<decltype(params)>) == 2) ? 1 : 2;
-                    apply_band<kT, kParts>(params, copy, mt, wl, pitch, cpr, a0, b0, rows_o, cols_o,
-                                           hv.decay, hv.lr, lane);
+                    apply_band<kT, kParts, kU>(params, copy, mt, wl, pitch, cpr, a0, b0, rows_o, cols_o,
+                                               hv.decay, hv.lr, lane);
                 } else {
 #pragma unroll
                     for (int t = 0; t < kT; ++t) {
@@ -967,12 +993,26 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                 }
             });
         };
-        if (!args.fuse)
-            bands(static_cast<float*>(nullptr), nullptr, std::false_type{});
-        else if (args.param_bf16)
-            bands(static_cast<uint16_t*>(args.params), nullptr, std::true_type{});
-        else
-            bands(static_cast<float*>(args.params), args.model_copy, std::true_type{});
+        // O rows whose length is not a multiple of 4 (unsharded matrices only:
+        // sharded slices may start inside a group) update element by element in
+        // the 64/128-tile kernels.  The 256-tile kernels keep the aligned path
+        // alone: the second instance costs their other paths registers (spills),
+        // and they take the rows of 513..1024-long sides, where the per-element
+        // round trips are a smaller share of a tile's time.
+        const bool unaligned = TILE < 256 && (cols_o & 3) != 0 && mt.slice_len == mt.numel;
+        if (!args.fuse) {
+            bands(static_cast<float*>(nullptr), nullptr, std::false_type{}, std::false_type{});
+        } else if (!unaligned) {
+            if (args.param_bf16)
+                bands(static_cast<uint16_t*>(args.params), nullptr, std::true_type{}, std::false_type{});
+            else
+                bands(static_cast<float*>(args.params), args.model_copy, std::true_type{}, std::false_type{});
+        } else if constexpr (TILE < 256) {
+            if (args.param_bf16)
+                bands(static_cast<uint16_t*>(args.params), nullptr, std::true_type{}, std::true_type{});
+            else
+                bands(static_cast<float*>(args.params), args.model_copy, std::true_type{}, std::true_type{});
+        }
     }
 }
 
