@@ -14,8 +14,8 @@
 // applies 1 / ||U|| in its float32 epilogues -- in NS orientation, and writes
 // the workgroup's sum of squares of U (fixed order) for norm_kernel.  A wide or
 // square matrix keeps its orientation, and each workgroup streams a contiguous
-// run of the padded iterate; a tall one is handled in 64 x 64 tiles transposed
-// through LDS.  G and M are streamed with nontemporal accesses.  One pass
+// run of the padded iterate; a tall one is handled in blocks of 32 x 128 (or
+// 64 x 64) elements of U transposed through LDS.  G and M are streamed with nontemporal accesses.  One pass
 // replaces front + cast.
 //
 // cast_kernel: one workgroup per 64 x 64 tile of the padded NS-orientation
@@ -131,7 +131,8 @@ __global__ __launch_bounds__(256) void front_cast_kernel(const MatInfo* __restri
                                                          float* __restrict__ partial) {
     constexpr int T = kCastTile;
     constexpr int kIters = T * T / 4 / 256;  // 4-element groups per thread
-    __shared__ float tile[T][T + 1];
+    // tall blocks: TR rows of TC + 1 floats (TR = 64 or 32)
+    __shared__ float tile[T * (T + 1)];
     __shared__ float wsum[4];
     const int blk = blockIdx.x;
     const int mi = owner_of(prefix, n, blk);
@@ -205,6 +206,51 @@ __global__ __launch_bounds__(256) void front_cast_kernel(const MatInfo* __restri
         else
             store_x4(x + mt.x_off + at, v);
     };
+    // Tall: workgroup t takes a block of TR rows x TC = 4096 / TR columns of U
+    // (iterate tile (ti, tj): TC iterate rows by TR iterate columns), read along
+    // U's rows (TC / 4 consecutive threads per row) and transposed through LDS.
+    // Consecutive workgroups take consecutive ti, i.e. neighbouring column
+    // blocks of the same TR rows of U.  TR = 32 (512-byte runs of G and M)
+    // where the iterate's padded row count is a multiple of 128, else 64.
+    const int tall_rows = (mt.rp % 128 == 0) ? 32 : 64;
+    auto tall_in = [&](auto tr_tag) {
+        constexpr int TR = decltype(tr_tag)::value, TC = T * T / TR, kSegs = TC / 4;
+        const int nti = mt.rp / TC;
+        const int tj = t / nti, ti = t % nti;
+        const int ur0 = tj * TR, uc0 = ti * TC;  // block origin in U's (R x C) coordinates
+        float gv[kIters][4], mv[kIters][4];
+#pragma unroll
+        for (int it = 0; it < kIters; ++it) {
+            const int seg = it * 256 + int(threadIdx.x);
+            load4(ur0 + seg / kSegs, uc0 + (seg % kSegs) * 4, gv[it], mv[it]);
+        }
+#pragma unroll
+        for (int it = 0; it < kIters; ++it) {
+            const int seg = it * 256 + int(threadIdx.x);
+            const int rr = seg / kSegs, c4 = (seg % kSegs) * 4;
+            float uv[4];
+            update4(ur0 + rr, uc0 + c4, gv[it], mv[it], uv);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                tile[rr * (TC + 1) + c4 + q] = uv[q];
+                ss = ss + uv[q] * uv[q];
+            }
+        }
+    };
+    // X[i][j], i = ti*TC + a, j = tj*TR + b = U[j][i] = block element (b, a); each
+    // thread writes 4 consecutive elements of a row
+    auto tall_out = [&](auto tr_tag) {
+        constexpr int TR = decltype(tr_tag)::value, TC = T * T / TR;
+        const int nti = mt.rp / TC;
+        const int tj = t / nti, ti = t % nti;
+        for (int idx = threadIdx.x; idx < T * T / 4; idx += 256) {
+            const int a = idx / (TR / 4), b = (idx % (TR / 4)) * 4;
+            float v[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = tile[(b + q) * (TC + 1) + a];
+            store_iter4(int64_t(ti * TC + a) * mt.cp + tj * TR + b, v);
+        }
+    };
     if (!tall) {
         // The iterate has U's own orientation: workgroup t takes the 4096
         // consecutive elements [4096 t, 4096 t + 4096) of the row-major rp x cp
@@ -228,33 +274,10 @@ __global__ __launch_bounds__(256) void front_cast_kernel(const MatInfo* __restri
             for (int q = 0; q < 4; ++q) ss = ss + uv[q] * uv[q];
             store_iter4(base + (it * 256 + int(threadIdx.x)) * 4, uv);
         }
+    } else if (tall_rows == 32) {
+        tall_in(std::integral_constant<int, 32>{});
     } else {
-        // Tall: workgroup t takes the 64 x 64 tile (ti, tj) of the iterate, read
-        // along U's rows (64 rows x 16 four-element segments, 16 consecutive
-        // threads per row) and transposed through LDS.  Consecutive workgroups
-        // take consecutive ti, i.e. neighbouring column blocks of the same 64
-        // rows of U.
-        const int nti = mt.rp / T;
-        const int tj = t / nti, ti = t % nti;
-        const int ur0 = tj * T, uc0 = ti * T;  // tile origin in U's (R x C) coordinates
-        float gv[kIters][4], mv[kIters][4];
-#pragma unroll
-        for (int it = 0; it < kIters; ++it) {
-            const int seg = it * 256 + int(threadIdx.x);
-            load4(ur0 + (seg >> 4), uc0 + (seg & 15) * 4, gv[it], mv[it]);
-        }
-#pragma unroll
-        for (int it = 0; it < kIters; ++it) {
-            const int seg = it * 256 + int(threadIdx.x);
-            const int rr = seg >> 4, c4 = (seg & 15) * 4;
-            float uv[4];
-            update4(ur0 + rr, uc0 + c4, gv[it], mv[it], uv);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                tile[rr][c4 + q] = uv[q];
-                ss = ss + uv[q] * uv[q];
-            }
-        }
+        tall_in(std::integral_constant<int, 64>{});
     }
     // deterministic block sum: fixed shuffle tree, then the 4 wave sums in order
     for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
@@ -262,17 +285,10 @@ __global__ __launch_bounds__(256) void front_cast_kernel(const MatInfo* __restri
     __syncthreads();
     if (threadIdx.x == 0) partial[blk] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
     if (tall) {
-        // X[i][j], i = ti*T + a, j = tj*T + b = U[j][i] = tile[b][a]; each thread
-        // writes 4 consecutive elements of a row
-        const int nti = mt.rp / T;
-        const int tj = t / nti, ti = t % nti;
-        for (int idx = threadIdx.x; idx < T * T / 4; idx += 256) {
-            const int a = idx / (T / 4), b = (idx % (T / 4)) * 4;
-            float v[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = tile[b + q][a];
-            store_iter4(int64_t(ti * T + a) * mt.cp + tj * T + b, v);
-        }
+        if (tall_rows == 32)
+            tall_out(std::integral_constant<int, 32>{});
+        else
+            tall_out(std::integral_constant<int, 64>{});
     }
 }
 
