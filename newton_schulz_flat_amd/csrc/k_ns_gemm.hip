@@ -966,9 +966,11 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(Ns
                 const int pitch = tall ? kPT : kPN;
                 const int a0 = tall ? c0w : r0w + i * 32, b0 = tall ? r0w + i * 32 : c0w;
                 if constexpr (kFuse) {
-                    // whole bands of bfloat16 weights in the bfloat16 kernels, else halves
+                    // whole bands in the 64/128-tile kernels and for bfloat16 weights in
+                    // the bfloat16 kernels; halves of float32 bands in the 256-tile ones
+                    // (their registers)
                     constexpr int kParts =
-                        (BF16 && sizeof(std::remove_pointer_t<decltype(params)>) == 2) ? 1 : 2;
+                        (TILE < 256 || (BF16 && sizeof(std::remove_pointer_t<decltype(params)>) == 2)) ? 1 : 2;
                     apply_band<kT, kParts, kU>(params, copy, mt, wl, pitch, cpr, a0, b0, rows_o, cols_o,
                                                hv.decay, hv.lr, lane);
                 } else {
