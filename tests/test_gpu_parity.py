@@ -286,6 +286,52 @@ def test_step_equals_composition(nsf, torch, mode, dtype, shards):
     assert np.array_equal(bits(host(params)), bits(host(p2)))
 
 
+# Tall matrices through both block shapes of the front pass (32 x 128 blocks of
+# U where the iterate's padded row count is a multiple of 128, else 64 x 64) in
+# the 64-, 128- and 256-tile classes; all but one have rows whose length is not
+# a multiple of 4, which the fused update of the 64/128-tile kernels handles
+# element by element.
+TALL_SHAPES = [(900, 771), (700, 301), (650, 201), (400, 150), (333, 97), (1030, 1029),
+               (512, 200)]
+
+
+@pytest.mark.parametrize("mode", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_tall_blocks_and_unaligned_rows(nsf, torch, mode, dtype):
+    """M bit for bit against the same-order reference, O against the fp64 oracle,
+    and the whole step bit for bit against its composition (whose apply kernel
+    matches the same-order reference bit for bit)."""
+    descs, off = [], 0
+    for r, c in TALL_SHAPES:
+        descs.append(wlm.Desc(off, r, c, off))
+        off = (off + r * c + 63) // 64 * 64 + 64
+    wl = wlm.Workload("tall_blocks", descs, dtype, off, off, 0.02, 1e-3,
+                      [f"m{i}" for i in range(len(descs))])
+    say("tall blocks / unaligned rows", mode, dtype, TALL_SHAPES)
+    params, grads, mom = _step_copies(wl, torch, momentum_std=1e-3)
+    w0, m0, gh = host(params), host(mom), host(grads)
+    p1, m1 = params.clone(), mom.clone()
+    nsf.muon_step(p1, grads, m1, descs, H["lr"], H["weight_decay"], H["beta"], mode=mode)
+    p2, m2 = params.clone(), mom.clone()
+    u = torch.zeros_like(grads)
+    o = torch.zeros_like(grads)
+    nsf.muon_momentum(grads, m2, u, descs, H["beta"], True)
+    nsf.muon_orthogonalize(u, o, descs, mode=mode)
+    nsf.muon_apply(p2, o, descs, H["lr"], H["weight_decay"])
+    gpu_sync(torch)
+    oh, w1, w2 = host(o), host(p1), host(p2)
+    assert np.array_equal(bits(host(m1)), bits(host(m2)))
+    assert np.array_equal(bits(w1), bits(w2))
+    for d in descs:
+        want_m, want_u = so.front(mat(gh, d), mat(m0, d), H["beta"], True)
+        assert np.array_equal(bits(mat(host(m1), d)), bits(want_m)), (d.rows, d.cols)
+        want_o = mo.newton_schulz(want_u.astype(np.float64), H["ns_steps"])
+        err = rel_fro(mat(oh, d), want_o)
+        assert err <= TOL[mode], (d.rows, d.cols, err)
+        want_w = so.apply(mat(w0, d).ravel(), mat(oh, d).ravel(), H["lr"], H["weight_decay"], dtype)
+        assert np.array_equal(bits(mat(w1, d).ravel()), bits(want_w)), (d.rows, d.cols)
+
+
 @pytest.mark.parametrize("mode", ["f32", "bf16"])
 def test_three_steps_against_oracle(nsf, torch, mode):
     """Three consecutive steps (so M != 0): M bit for bit against the same-order
