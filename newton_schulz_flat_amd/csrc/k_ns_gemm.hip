@@ -83,6 +83,10 @@ template <int TILE, bool BF16>
 struct Geo {
     static constexpr int kWaves = (TILE == 256 && BF16) ? 8 : 4;
     static constexpr int kThreads = kWaves * 64;
+    // waves per SIMD the registers must allow: two 128-tile workgroups share a
+    // CU (their LDS fits twice), so that one's epilogue overlaps the other's
+    // main loop
+    static constexpr int kMinWaves = TILE == 128 ? 2 : 1;
     static constexpr int kOp = TILE * kLdsStride;       // bytes of one staged operand tile
     static constexpr int kWm = TILE / 2;                 // wave tile rows
     static constexpr int kWn = TILE / (kWaves / 2);      // wave tile columns
@@ -384,7 +388,8 @@ __device__ __forceinline__ void store_q(unsigned char* dst, const u32x4 (&pb)[kL
 }
 
 template <int TILE, bool BF16, int STAGE>
-__global__ __launch_bounds__((Geo<TILE, BF16>::kThreads)) void ns_gemm_kernel(NsArgs args) {
+__global__ __launch_bounds__((Geo<TILE, BF16>::kThreads), (Geo<TILE, BF16>::kMinWaves)) void ns_gemm_kernel(
+    NsArgs args) {
     using TE = std::conditional_t<BF16, uint16_t, float>;
     using G = Geo<TILE, BF16>;
     constexpr int kEs = BF16 ? 2 : 4;
