@@ -54,8 +54,6 @@ __global__ __launch_bounds__(kNormThreads) void norm_kernel(const MatInfo* __res
     if (threadIdx.x == 0) inv[mi] = 1.0f / (sqrtf(red[0]) + kNormEps);
 }
 
-__device__ __forceinline__ void store_x(float* p, float v) { *p = v; }
-__device__ __forceinline__ void store_x(uint16_t* p, float v) { *p = bf16_rne(v); }
 __device__ __forceinline__ void store_x4(float* p, const float v[4]) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }

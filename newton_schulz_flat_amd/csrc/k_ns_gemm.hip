@@ -95,27 +95,8 @@ struct Geo {
     static constexpr int kLoads = TILE / kRowsPerPass;   // 16-byte loads per thread per operand
 };
 
-__device__ __forceinline__ float load_e(const float* p) { return *p; }
-__device__ __forceinline__ float load_e(const uint16_t* p) { return bf16_to_f32(*p); }
-__device__ __forceinline__ void store_e(float* p, float v) { *p = v; }
-__device__ __forceinline__ void store_e(uint16_t* p, float v) { *p = bf16_rne(v); }
-
-__device__ __forceinline__ void load4(const float* p, float v[4]) {
-    const float4 t = *reinterpret_cast<const float4*>(p);
-    v[0] = t.x, v[1] = t.y, v[2] = t.z, v[3] = t.w;
-}
-__device__ __forceinline__ void load4(const uint16_t* p, float v[4]) {
-    const uint2 t = *reinterpret_cast<const uint2*>(p);
-    v[0] = __uint_as_float(t.x << 16), v[1] = __uint_as_float(t.x & 0xffff0000u);
-    v[2] = __uint_as_float(t.y << 16), v[3] = __uint_as_float(t.y & 0xffff0000u);
-}
 __device__ __forceinline__ void store4(float* p, const float v[4]) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-}
-__device__ __forceinline__ void store4(uint16_t* p, const float v[4]) {
-    const uint32_t lo = uint32_t(bf16_rne(v[0])) | (uint32_t(bf16_rne(v[1])) << 16);
-    const uint32_t hi = uint32_t(bf16_rne(v[2])) | (uint32_t(bf16_rne(v[3])) << 16);
-    *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
 }
 
 // Raw (undecoded) 4-element operand vectors: loaded in batches so that one
