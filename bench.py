@@ -138,8 +138,9 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs the Muon step on one GPU only; the multi-GPU "
-              "owner-compute path is not built, so --gpus must be 1", file=sys.stderr)
+        print("bench.py: the Muon step here runs on one GPU; the multi-GPU owner-compute "
+              "path (exchanges of update slices between ranks) is not implemented, so "
+              "--gpus must be 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
