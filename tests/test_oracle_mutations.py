@@ -40,6 +40,8 @@ PIN_TESTS = [
     lambda: pins.test_momentum_constant_gradient_closed_form(False),
     pins.test_zero_gradient_is_pure_decay_over_steps,
     pins.test_update_direction_opposes_gradient_1x1,
+    pins.test_decay_then_update_order_exact_1x1,
+    pins.test_hyperparameters_are_float32_values,
     lambda: pins.test_newton_schulz_1x1_exact(1e-7),
     lambda: pins.test_newton_schulz_singular_value_closed_form((6, 10), 5),
     lambda: pins.test_newton_schulz_singular_value_closed_form((10, 6), 5),
@@ -72,6 +74,9 @@ MUTATIONS = {
                               lambda g, m, b, n: g + m if n else m.copy()),
     "decay_without_lr": ("apply_update", lambda w, o, lr, wd: w * (1 - wd) - lr * o),
     "update_sign": ("apply_update", lambda w, o, lr, wd: w * (1 - lr * wd) + lr * o),
+    "decay_after_update": ("apply_update", lambda w, o, lr, wd: (w - lr * o) * (1 - lr * wd)),
+    "decay_on_update_not_weight": ("apply_update", lambda w, o, lr, wd: w - lr * o * (1 - lr * wd)),
+    "hyper_not_f32_rounded": ("as_f32_value", lambda x: float(x)),
     "transposed_gram": ("newton_schulz", _ns_variant(transposed_gram=True)),
     "poly_on_right_of_square_gram": ("newton_schulz", _ns_variant(poly_right=True)),
     "spectral_norm": ("newton_schulz", _ns_variant(spectral_norm=True)),

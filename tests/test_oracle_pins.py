@@ -100,6 +100,51 @@ def test_lr_zero_leaves_weights():
     assert np.array_equal(p64, w.astype(np.float64))
 
 
+def test_decay_then_update_order_exact_1x1():
+    """W, O and wd all non-zero: W1 = W (1 - lr wd) - lr O, exactly in rationals.
+
+    Decay acts on the old weight only (decoupled decay applied in
+    _compute_momentum_inputs before _apply_local_updates subtracts the
+    update).  Decaying after the update, (W - lr O)(1 - lr wd), differs by
+    lr^2 wd O ~ 0.04 here.  Every hyperparameter is exact in float32.
+    """
+    g, w0, lr, wd = 0.25, 0.5, 0.5, 0.25
+    p64, _, upd = mo.muon_step(np.array([w0], np.float32), np.array([g], np.float32),
+                               np.zeros(1, np.float32), [mo.MatrixDesc(0, 1, 1, 0)],
+                               lr=lr, weight_decay=wd, beta=0.0, nesterov=False)
+    o = quintic_iter(Fraction(g) / (Fraction(g) + Fraction(EPS)), 5)
+    want = Fraction(w0) * (1 - Fraction(lr) * Fraction(wd)) - Fraction(lr) * o
+    assert abs(Fraction(upd[0][0, 0]) - o) < Fraction(1, 10 ** 14)
+    assert abs(Fraction(p64[0]) - want) < Fraction(1, 10 ** 14)
+
+
+#: float32 roundings of the hyperparameters, written out by hand (24-bit
+#: significands of 0.02, 0.1 and 0.95).
+F32_OF_0_02 = float.fromhex("0x1.47ae14p-6")
+F32_OF_0_1 = float.fromhex("0x1.99999ap-4")
+F32_OF_0_95 = float.fromhex("0x1.e66666p-1")
+
+
+def test_hyperparameters_are_float32_values():
+    """The oracle works with the float32 values the device receives.
+
+    Expected values use hand-written float32 constants, not the oracle's
+    rounding helper: zero gradient and zero momentum give O = 0 and
+    W1 = W (1 - lr wd) with lr = wd = fl32(0.1); zero gradient and M0 = 1 give
+    M1 = fl32(0.95).  Products of two 24-bit significands are exact in float64,
+    so both comparisons are exact.
+    """
+    assert mo.as_f32_value(0.02) == F32_OF_0_02
+    assert mo.as_f32_value(0.95) == F32_OF_0_95
+    d = [mo.MatrixDesc(0, 1, 1, 0)]
+    p64, _, _ = mo.muon_step(np.array([1.0], np.float32), np.zeros(1, np.float32),
+                             np.zeros(1, np.float32), d, lr=0.1, weight_decay=0.1, beta=0.5)
+    assert p64[0] == 1.0 - F32_OF_0_1 * F32_OF_0_1
+    _, m64, _ = mo.muon_step(np.array([1.0], np.float32), np.zeros(1, np.float32),
+                             np.ones(1, np.float32), d, lr=0.0, weight_decay=0.0, beta=0.95)
+    assert m64[0] == F32_OF_0_95
+
+
 def test_update_direction_opposes_gradient_1x1():
     """1x1, W = 0, g > 0: W1 = -lr f^5(g/(g+eps)) exactly in rationals."""
     g = 0.25
