@@ -37,7 +37,13 @@
  * as U itself (rounded to the Newton-Schulz type) and the normalization is
  * applied in float32 inside the first iteration: A0 = inv^2 (U U^T),
  * X1 = inv (a U + B0 U), inv = 1 / (||U||_F + 1e-7) -- the same iterates as
- * X0 = U / (||U||_F + 1e-7), with one rounding fewer.  With ns_steps == 0,
+ * X0 = U / (||U||_F + 1e-7), with one rounding fewer.  Rank-deficient inputs:
+ * the exact O lies in U's column and row spaces, and that part is computed to
+ * the mode's accuracy; in U's null space each iteration multiplies rounding
+ * noise by a = 3.4445, so O also carries a component there, about a^5 times
+ * the products' rounding error: below 3e-4 of ||O|| in float32, but of the
+ * order of ||O|| itself with bfloat16 iterates (use MUON_GEMM_F32 for inputs
+ * of very low rank).  With ns_steps == 0,
  * O = fl(s * X0) with X0 rounded to the Newton-Schulz type.  O = fl(s * x)
  * in float32.  Results are deterministic and do not depend on the order of
  * descriptors; muon_step equals muon_apply(muon_orthogonalize(muon_momentum))
@@ -45,20 +51,36 @@
  *
  * Buffers.  All buffer pointers are device pointers allocated by the caller,
  * who keeps ownership.  Descriptor arrays are host memory read during the
- * call.  The workspace is caller-owned device memory of at least
- * muon_workspace_bytes() bytes, 256-byte aligned; its contents are undefined
- * after a call.  Calls that share a workspace must be ordered on one stream.
+ * call.  The workspace is caller-owned device memory, 256-byte aligned; its
+ * contents are undefined after a call.  Calls that share a workspace must be
+ * ordered on one stream.  With muon_workspace_bytes() bytes every matrix is
+ * orthogonalized in one wave; a smaller workspace of at least
+ * muon_workspace_min_bytes() bytes runs the matrices in waves, each wave's
+ * intermediates fitting the workspace (the pages' optimizer likewise works
+ * through its buffers one at a time on the caller's stream, FsdpMuon class
+ * docstring).  Results do not depend on the wave split, bit for bit.
  *
  * Execution.  All work is enqueued on `stream` (0 = the null stream) and the
  * call returns without waiting for it.  The first call with a new descriptor
- * set (per device and GEMM mode) builds a launch plan and uploads its tables
- * (one device allocation, kept until the process ends or the plan is evicted
- * from a 32-entry cache); later calls with the same descriptors allocate
- * nothing and do not synchronize the host.
+ * set (per device, GEMM mode and -- when it runs in waves -- workspace size)
+ * builds a launch plan and uploads its tables: one device allocation and a
+ * stream synchronization, so make that call outside graph capture and while
+ * no stream of the process is being captured in global mode.  Later calls
+ * with the same set allocate nothing and do not synchronize the host.  Plans
+ * stay in a 64-entry least-recently-used cache; a plan used while its stream
+ * is being captured into a HIP graph is pinned (never evicted, kept until the
+ * process ends), since the graph keeps pointers to its tables.  An evicted
+ * plan's tables are freed after a device synchronization.
  *
- * Errors.  Every entry point returns MUON_OK (0) or a negative muon_status_t.
- * Every check except MUON_ERR_HIP runs before anything is enqueued, so a
- * failed call leaves every buffer untouched.  muon_last_error() returns a
+ * Errors.  The pages' optimizer validates its parameter-to-group mapping up
+ * front and raises rather than run on a bad mapping (FsdpMuon._validate_parameter_groups
+ * on the page "core.distributed.fsdp.src.megatron_fsdp.experimental.muon";
+ * the review answer on the page "feat(fsdp): expose HSDP and HFSDP through
+ * the MFSDP v2 adapter" that an unsupported layout raises instead of being
+ * silently mis-mapped).  Here every entry point returns MUON_OK (0) or a
+ * negative muon_status_t instead of raising: nothing is thrown across the
+ * ABI.  Every check except MUON_ERR_HIP runs before anything is enqueued, so
+ * a failed call leaves every buffer untouched.  muon_last_error() returns a
  * thread-local message describing the last failure of this thread.  Values
  * that are NaN or infinite inside the buffers are not checked: they propagate.
  */
@@ -124,13 +146,21 @@ enum { MUON_DTYPE_F32 = 0, MUON_DTYPE_BF16 = 1 };
 /* Arithmetic of the Newton-Schulz chain. */
 enum { MUON_GEMM_BF16_MFMA = 0, MUON_GEMM_F32 = 1 };
 
-/* Bytes of device workspace that muon_step / muon_orthogonalize need for
- * these descriptors and GEMM mode (the plan-building analogue of the owner
- * assignment "computed during initialization" in FsdpMuon).  Host-only: makes
- * no HIP call.  Validates the descriptors' shapes (not their bounds).
- * out_bytes: host pointer receiving the size. */
+/* Bytes of device workspace with which muon_step / muon_orthogonalize run
+ * these descriptors in one wave, for this GEMM mode (the plan-building
+ * analogue of the owner assignment "computed during initialization" in
+ * FsdpMuon).  Host-only: makes no HIP call.  Validates the descriptors' shapes
+ * (not their bounds).  out_bytes: host pointer receiving the size. */
 int muon_workspace_bytes(const muon_matrix_desc_t* descs, int64_t n, int gemm_mode,
                          size_t* out_bytes);
+
+/* Smallest workspace with which the descriptors run at all: the largest
+ * single matrix's intermediates.  Between this and muon_workspace_bytes() the
+ * matrices run in waves whose intermediates fit the workspace given (the
+ * FsdpMuon class docstring: the step processes one buffer's updates at a time
+ * on the caller's stream).  Host-only, same validation as muon_workspace_bytes. */
+int muon_workspace_min_bytes(const muon_matrix_desc_t* descs, int64_t n, int gemm_mode,
+                             size_t* out_bytes);
 
 /* The whole step ("Opt step" steps 1, 2, 4, 6 of PR #6425; FsdpMuon.step).
  *   params        device, n_param_elems elements of param_dtype; updated in place.
@@ -139,7 +169,8 @@ int muon_workspace_bytes(const muon_matrix_desc_t* descs, int64_t n, int gemm_mo
  *   descs, n      host array of n descriptors (n == 0 is a no-op).
  *   lr, weight_decay, beta  finite float32 scalars.
  *   nesterov      0 or 1.   ns_steps  0..64.   gemm_mode  MUON_GEMM_*.
- *   workspace     device, >= muon_workspace_bytes(), 256-byte aligned.
+ *   workspace     device, 256-byte aligned, >= muon_workspace_min_bytes()
+ *                 (>= muon_workspace_bytes() for one wave).
  * The four buffers must not alias one another. */
 int muon_step(void* params, int param_dtype, int64_t n_param_elems, const float* grads,
               float* momentum, int64_t n_state_elems, const muon_matrix_desc_t* descs,
@@ -231,11 +262,20 @@ typedef struct muon_kernel_time {
 int muon_profile_begin(void);
 int muon_profile_end(muon_kernel_time_t* out, int max_entries, int* n_entries);
 
-/* Static name of a status code ("MUON_OK", "MUON_ERR_BAD_SHAPE", ...). */
+/* Static name of a status code ("MUON_OK", "MUON_ERR_BAD_SHAPE", ...): the
+ * kind of a rejected call, which the pages' optimizer reports by raising from
+ * its up-front validation (FsdpMuon._validate_parameter_groups, page
+ * "core.distributed.fsdp.src.megatron_fsdp.experimental.muon"; "raise rather
+ * than mis-map", review answers on the page "feat(fsdp): expose HSDP and
+ * HFSDP through the MFSDP v2 adapter").  Any int is accepted; unknown codes
+ * give "MUON_ERR_UNKNOWN".  The string is static: never free it. */
 const char* muon_status_string(int status);
 
-/* Message of the calling thread's last failure ("" if none); valid until the
- * thread's next call into this library. */
+/* Message of the calling thread's last failure ("" if none): the text the
+ * pages' validation would raise with (same passages as muon_status_string),
+ * naming the offending descriptor, buffer or argument.  Thread-local, owned
+ * by the library, valid until the thread's next failing call into this
+ * library; never free it.  Successful calls leave it unchanged. */
 const char* muon_last_error(void);
 
 #ifdef __cplusplus

@@ -15,7 +15,8 @@ Entry points (same names as the C ABI):
 ``muon_momentum``       momentum update and orthogonalization input only
 ``muon_orthogonalize``  Newton-Schulz orthogonalization (with shape scale) only
 ``muon_apply``          decoupled decay and update, scattered into slices
-``muon_workspace_bytes``
+``muon_workspace_bytes``      workspace for one wave
+``muon_workspace_min_bytes``  smallest workspace (the matrices then run in waves)
 
 Descriptors are objects with ``offset, rows, cols`` and optionally
 ``param_offset`` (default ``offset``), ``shard_stride`` (0), ``n_shards`` (1)
@@ -39,7 +40,7 @@ MUON_GEMM_F32 = 1
 _MODES = {"bf16": MUON_GEMM_BF16_MFMA, "f32": MUON_GEMM_F32}
 
 #: C names of every exported entry point (mirrors include/muon_step.h).
-EXPORTS = ("muon_workspace_bytes", "muon_step", "muon_step_grouped", "muon_momentum",
+EXPORTS = ("muon_workspace_bytes", "muon_workspace_min_bytes", "muon_step", "muon_step_grouped", "muon_momentum",
            "muon_orthogonalize", "muon_apply", "muon_profile_begin", "muon_profile_end",
            "muon_status_string", "muon_last_error")
 
@@ -84,6 +85,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                             ctypes.c_size_t)
     dp = ctypes.POINTER(MatrixDescC)
     lib.muon_workspace_bytes.argtypes = [dp, i64, i32, ctypes.POINTER(sz)]
+    lib.muon_workspace_min_bytes.argtypes = [dp, i64, i32, ctypes.POINTER(sz)]
     lib.muon_step.argtypes = [p, i32, i64, p, p, i64, dp, i64, f32, f32, f32, i32, i32, i32, p,
                               sz, p]
     lib.muon_step_grouped.argtypes = [p, i32, i64, p, p, p, i64, dp, i64, p, ctypes.c_int32, i32,
@@ -97,7 +99,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.muon_status_string.restype = ctypes.c_char_p
     lib.muon_last_error.argtypes = []
     lib.muon_last_error.restype = ctypes.c_char_p
-    for name in ("muon_workspace_bytes", "muon_step", "muon_step_grouped", "muon_momentum",
+    for name in ("muon_workspace_bytes", "muon_workspace_min_bytes", "muon_step", "muon_step_grouped", "muon_momentum",
                  "muon_orthogonalize", "muon_apply", "muon_profile_begin", "muon_profile_end"):
         getattr(lib, name).restype = i32
     _lib = lib
@@ -161,6 +163,7 @@ def _require(t, name, dtypes):
 
 
 def muon_workspace_bytes(descs, mode: str = "bf16") -> int:
+    """Workspace bytes with which the descriptors run in one wave."""
     lib = load_library()
     arr = descs_array(descs)
     out = ctypes.c_size_t(0)
@@ -168,24 +171,50 @@ def muon_workspace_bytes(descs, mode: str = "bf16") -> int:
     return out.value
 
 
+def muon_workspace_min_bytes(descs, mode: str = "bf16") -> int:
+    """Smallest workspace that runs the descriptors (in waves, one matrix or more each)."""
+    lib = load_library()
+    arr = descs_array(descs)
+    out = ctypes.c_size_t(0)
+    check(lib.muon_workspace_min_bytes(arr, _count(descs), _mode(mode), ctypes.byref(out)))
+    return out.value
+
+
+#: Default workspaces, one per (device, stream): calls sharing a workspace must
+#: be ordered on one stream.  Each is allocated on the stream it serves, so the
+#: caching allocator hands a replaced (smaller) one out again only in that
+#: stream's order.
 _workspaces: dict = {}
 
 
 def workspace_for(descs, mode: str, device):
-    """A cached uint8 workspace tensor of at least the needed size on ``device``."""
+    """A cached uint8 workspace of at least the one-wave size, for the current
+    stream of ``device``.  Not usable under graph capture (the graph would keep
+    a pointer that a later, larger set frees): pass an explicit workspace there."""
     import torch
+    dev = torch.device(device)
+    if torch.cuda.is_current_stream_capturing():
+        raise RuntimeError("pass an explicit workspace to calls made under graph capture")
+    stream = torch.cuda.current_stream(dev)
     need = muon_workspace_bytes(descs, mode)
-    key = torch.device(device)
+    key = (dev, stream.cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=key)
+        _workspaces.pop(key, None)
+        with torch.cuda.stream(stream):
+            ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         _workspaces[key] = ws
     return ws
 
 
 def muon_step(params, grads, momentum, descs, lr: float, weight_decay: float, beta: float,
               nesterov: bool = True, ns_steps: int = 5, mode: str = "bf16", workspace=None):
-    """One Muon step in place on ``params`` (f32 or bf16) and ``momentum`` (f32)."""
+    """One Muon step in place on ``params`` (f32 or bf16) and ``momentum`` (f32).
+
+    ``workspace``: a uint8 GPU tensor (default: a cached one per device and
+    stream, of the one-wave size).  A workspace smaller than
+    ``muon_workspace_bytes`` but at least ``muon_workspace_min_bytes`` runs the
+    matrices in waves that fit it, with identical results."""
     import torch
     _require(params, "params", (torch.float32, torch.bfloat16))
     _require(grads, "grads", (torch.float32,))

@@ -34,11 +34,13 @@ __device__ __forceinline__ float block_sum(float v, float* lds4) {
 
 // kMode 0: M <- beta M + G, U <- G + beta M (or M); partial sums of U^2.
 // kMode 1: partial sums of U^2 only (U given).
+// U element e of a matrix at offset off lives at u[e] (grads layout) or, with
+// u_compact, at u[e - off + u_off] (the workspace's compact U region).
 template <int kMode>
 __global__ __launch_bounds__(kEwThreads) void front_kernel(
     const MatInfo* __restrict__ mats, const int32_t* __restrict__ prefix, int n,
-    const float* __restrict__ g, float* __restrict__ m, float* __restrict__ u,
-    float* __restrict__ partial, Hyper h) {
+    const float* __restrict__ g, float* __restrict__ m, float* __restrict__ u_base,
+    int u_compact, float* __restrict__ partial, Hyper h) {
     __shared__ float lds4[4];
     const int blk = blockIdx.x;
     const int mi = owner_of(prefix, n, blk);
@@ -48,6 +50,8 @@ __global__ __launch_bounds__(kEwThreads) void front_kernel(
     const int64_t off = mats[mi].off;
     const int64_t end = off + mats[mi].numel;
     const int64_t base = off + int64_t(blk - mats[mi].chunk_begin) * kEwChunk;
+    // U element e (e counts from off, like G and M) is u_base[e + ud]
+    const int64_t ud = u_compact ? mats[mi].u_off - off : int64_t(0);
     float ss = 0.f;
 #pragma unroll
     for (int it = 0; it < kEwIters; ++it) {
@@ -71,9 +75,9 @@ __global__ __launch_bounds__(kEwThreads) void front_kernel(
                 } else {
                     uv = m1;
                 }
-                store4_stream(u + e, uv);
+                store4_stream(u_base + (e + ud), uv);
             } else {
-                uv = load4_stream(u + e);
+                uv = load4_stream(u_base + (e + ud));
             }
             ss += uv.x * uv.x;
             ss += uv.y * uv.y;
@@ -87,9 +91,9 @@ __global__ __launch_bounds__(kEwThreads) void front_kernel(
                     const float m1 = beta * m[k] + gk;
                     m[k] = m1;
                     uk = nesterov ? beta * m1 + gk : m1;
-                    u[k] = uk;
+                    u_base[k + ud] = uk;
                 } else {
-                    uk = u[k];
+                    uk = u_base[k + ud];
                 }
                 ss += uk * uk;
             }
@@ -120,16 +124,19 @@ __device__ __forceinline__ void store_w1(uint16_t* p, float v) { *p = bf16_rne(v
 
 // W1 = fl(W f); Wn = fl(W1 - fl(lr O)); element j of the flattened matrix
 // lives in slice j / slice_len at param offset poff + k pstride + j % slice_len.
+// O of the matrix at o[off ...] (grads layout) or, with o_compact, at
+// o[u_off ...] (the workspace's compact region).
 template <typename TW>
 __global__ __launch_bounds__(kEwThreads) void apply_kernel(
     const MatInfo* __restrict__ mats, const int32_t* __restrict__ prefix, int n,
-    TW* __restrict__ w, const float* __restrict__ o, Hyper h, uint16_t* __restrict__ copy) {
+    TW* __restrict__ w, const float* __restrict__ o, int o_compact, Hyper h,
+    uint16_t* __restrict__ copy) {
     const int blk = blockIdx.x;
     const int mi = owner_of(prefix, n, blk);
     const MatInfo& mt = mats[mi];
     const HyperVals hv = hyper_for(h, mt);
     const float decay = hv.decay, lr = hv.lr;
-    const int64_t numel = mt.numel, off = mt.off, poff = mt.poff;
+    const int64_t numel = mt.numel, off = o_compact ? mt.u_off : mt.off, poff = mt.poff;
     const int64_t slice = mt.slice_len, stride = mt.pstride;
     const bool sharded = slice != numel;
     const int64_t base = int64_t(blk - mt.chunk_begin) * kEwChunk;
@@ -169,11 +176,11 @@ __global__ __launch_bounds__(kEwThreads) void apply_kernel(
 }  // namespace
 
 hipError_t launch_front(const PlanView& p, const float* grads, float* momentum, float* u,
-                        float* partial, const Hyper& h, hipStream_t s) {
+                        bool compact, float* partial, const Hyper& h, hipStream_t s) {
     if (p.total_chunks == 0) return hipSuccess;
     LaunchTimer timer("front", s);
     front_kernel<0><<<dim3(unsigned(p.total_chunks)), dim3(kEwThreads), 0, s>>>(
-        p.mats, p.chunk_prefix, p.n, grads, momentum, u, partial, h);
+        p.mats, p.chunk_prefix, p.n, grads, momentum, u, compact ? 1 : 0, partial, h);
     return hipGetLastError();
 }
 
@@ -181,21 +188,24 @@ hipError_t launch_sumsq(const PlanView& p, const float* u, float* partial, hipSt
     if (p.total_chunks == 0) return hipSuccess;
     LaunchTimer timer("sumsq", s);
     front_kernel<1><<<dim3(unsigned(p.total_chunks)), dim3(kEwThreads), 0, s>>>(
-        p.mats, p.chunk_prefix, p.n, nullptr, nullptr, const_cast<float*>(u), partial, Hyper{});
+        p.mats, p.chunk_prefix, p.n, nullptr, nullptr, const_cast<float*>(u), 0, partial, Hyper{});
     return hipGetLastError();
 }
 
 hipError_t launch_apply(const PlanView& p, void* params, int param_dtype, const float* o,
-                        const Hyper& h, uint16_t* model_copy, hipStream_t s) {
+                        bool compact, const Hyper& h, uint16_t* model_copy, hipStream_t s) {
     if (p.total_chunks == 0) return hipSuccess;
     LaunchTimer timer("apply", s);
     const dim3 grid{static_cast<unsigned>(p.total_chunks)}, block{kEwThreads};
+    const int oc = compact ? 1 : 0;
     if (param_dtype == MUON_DTYPE_BF16)
         apply_kernel<uint16_t><<<grid, block, 0, s>>>(p.mats, p.chunk_prefix, p.n,
-                                                      static_cast<uint16_t*>(params), o, h, nullptr);
+                                                      static_cast<uint16_t*>(params), o, oc, h,
+                                                      nullptr);
     else
         apply_kernel<float><<<grid, block, 0, s>>>(p.mats, p.chunk_prefix, p.n,
-                                                   static_cast<float*>(params), o, h, model_copy);
+                                                   static_cast<float*>(params), o, oc, h,
+                                                   model_copy);
     return hipGetLastError();
 }
 

@@ -65,12 +65,15 @@ __device__ __forceinline__ void store_x4(uint16_t* p, const float v[4]) {
 __device__ __forceinline__ float rounded(float v, float*) { return v; }
 __device__ __forceinline__ float rounded(float v, uint16_t*) { return bf16_to_f32(bf16_rne(v)); }
 
+// U (and O) of a matrix at its offset in the grads layout, or (compact) at its
+// u_off in the workspace's compact region.
 template <typename TX>
 __global__ __launch_bounds__(256) void cast_kernel(const MatInfo* __restrict__ mats,
                                                    const int32_t* __restrict__ prefix, int n,
                                                    const float* u,  // may equal o_direct
                                                    const float* __restrict__ inv,
-                                                   TX* __restrict__ x, float* o_direct) {
+                                                   TX* __restrict__ x, float* o_direct,
+                                                   int compact) {
     constexpr int T = kCastTile;
     __shared__ float tile[T][T + 1];
     const int blk = blockIdx.x;
@@ -84,7 +87,8 @@ __global__ __launch_bounds__(256) void cast_kernel(const MatInfo* __restrict__ m
     const int ur0 = tall ? tj * T : ti * T;
     const int uc0 = tall ? ti * T : tj * T;
     const float scale_inv = inv[mi];
-    const float* um = u + mt.off;
+    const int64_t uoff = compact ? mt.u_off : mt.off;
+    const float* um = u + uoff;
     for (int idx = threadIdx.x; idx < T * T; idx += 256) {
         const int rr = idx / T, cc = idx % T;
         const int gr = ur0 + rr, gc = uc0 + cc;
@@ -95,7 +99,7 @@ __global__ __launch_bounds__(256) void cast_kernel(const MatInfo* __restrict__ m
     __syncthreads();
     if (o_direct != nullptr) {
         // No iterations: O = fl(s * X0), X0 rounded to the storage type.
-        float* om = o_direct + mt.off;
+        float* om = o_direct + uoff;
         for (int idx = threadIdx.x; idx < T * T; idx += 256) {
             const int rr = idx / T, cc = idx % T;
             const int gr = ur0 + rr, gc = uc0 + cc;
@@ -331,7 +335,7 @@ hipError_t launch_front_cast(const PlanView& p, const float* grads, float* momen
 }
 
 hipError_t launch_cast(const PlanView& p, const float* u, const float* inv, void* ws,
-                       float* o_direct, hipStream_t s) {
+                       float* o_direct, bool compact, hipStream_t s) {
     if (p.total_cast == 0) return hipSuccess;
     LaunchTimer timer("cast", s);
     unsigned char* w = static_cast<unsigned char*>(ws);
@@ -339,11 +343,11 @@ hipError_t launch_cast(const PlanView& p, const float* u, const float* inv, void
     if (p.gemm_mode == MUON_GEMM_F32)
         cast_kernel<float><<<grid, block, 0, s>>>(p.mats, p.cast_prefix, p.n, u, inv,
                                                   reinterpret_cast<float*>(w + p.ws.x[0]),
-                                                  o_direct);
+                                                  o_direct, compact ? 1 : 0);
     else
         cast_kernel<uint16_t><<<grid, block, 0, s>>>(p.mats, p.cast_prefix, p.n, u, inv,
                                                      reinterpret_cast<uint16_t*>(w + p.ws.x[0]),
-                                                     o_direct);
+                                                     o_direct, compact ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -884,7 +884,7 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads), (Geo<TILE, BF16>::kMin
         // stored, or (fused apply) used at once to update the weights.  Each
         // 32-row band of the wave's sub-tile is staged in a wave-private LDS region
         // in O's own orientation, then written out along O's rows.
-        float* om = args.o + mt.off;
+        float* om = args.fuse ? nullptr : args.o + mt.off;  // O is not stored when fused
         const float sc = mt.scale;
         const int r = mt.r, c = mt.c;
         const bool tall = mt.tall != 0;

@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstring>
 #include <new>
+#include <vector>
 
 #include <hip/hip_runtime.h>
 
@@ -72,19 +73,27 @@ int check_null(const void* p, const char* name, Status* st) {
     return MUON_OK;
 }
 
-int check_workspace(const void* ws, size_t have, size_t need, Status* st) {
-    if (need == 0) return MUON_OK;
+// The workspace must hold the largest single-matrix wave (need_min).  When it
+// holds the whole set (need_full), everything runs in one wave (*capacity = 0);
+// otherwise the set runs in waves of at most `have` bytes each.
+int check_workspace(const void* ws, size_t have, size_t need_full, size_t need_min,
+                    size_t* capacity, Status* st) {
+    *capacity = 0;
+    if (need_full == 0) return MUON_OK;
     if (ws == nullptr) return check_null(ws, "workspace", st);
     if (reinterpret_cast<uintptr_t>(ws) % muon::kWsAlign != 0) {
         st->code = MUON_ERR_MISALIGNED;
         snprintf(st->msg, sizeof(st->msg), "workspace is not %zu-byte aligned", muon::kWsAlign);
         return st->code;
     }
-    if (have < need) {
+    if (have < need_min) {
         st->code = MUON_ERR_WORKSPACE_TOO_SMALL;
-        snprintf(st->msg, sizeof(st->msg), "workspace has %zu bytes, needs %zu", have, need);
+        snprintf(st->msg, sizeof(st->msg),
+                 "workspace has %zu bytes; the largest matrix alone needs %zu (%zu for one wave)",
+                 have, need_min, need_full);
         return st->code;
     }
+    if (have < need_full) *capacity = have;
     return MUON_OK;
 }
 
@@ -129,8 +138,9 @@ int run_step(Status& st, void* params, int param_dtype, int64_t n_param_elems, v
         snprintf(st.msg, sizeof(st.msg), "model_copy is not 16-byte aligned");
         return finish(st);
     }
-    const size_t need = muon::workspace_bytes_for(descs, n, gemm_mode);
-    TRY(check_workspace(workspace, workspace_bytes, need, &st));
+    size_t capacity = 0;
+    TRY(check_workspace(workspace, workspace_bytes, muon::workspace_bytes_for(descs, n, gemm_mode),
+                        muon::min_workspace_bytes_for(descs, n, gemm_mode), &capacity, &st));
     const muon::Range ranges[6] = {
         {params, param_bytes(param_dtype, n_param_elems), "params"},
         {grads, size_t(n_state_elems) * 4, "grads"},
@@ -140,33 +150,57 @@ int run_step(Status& st, void* params, int param_dtype, int64_t n_param_elems, v
         {model_copy, model_copy ? size_t(n_param_elems) * 2 : 0, "model_copy"}};
     TRY(muon::check_no_alias(ranges, 6, &st));
 
-    std::shared_ptr<const muon::PlanStore> plan;
-    TRY(muon::get_plan(descs, n, gemm_mode, stream, &plan, &st));
-    const muon::PlanView& p = muon::view_of(*plan);
-    unsigned char* ws = static_cast<unsigned char*>(workspace);
-    float* u = reinterpret_cast<float*>(ws + p.ws.u);
-    float* partial = reinterpret_cast<float*>(ws + p.ws.partial);
-    float* inv = reinterpret_cast<float*>(ws + p.ws.inv);
-    uint16_t* copy = static_cast<uint16_t*>(model_copy);
-    if (ns_steps > 0) {
-        // momentum, input and first iterate in one pass; the norm is folded into
-        // iteration 0, and the last iteration applies the update itself (same
-        // roundings as the apply phase)
-        TRY_HIP(muon::launch_front_cast(p, grads, momentum, nullptr, h, ws, partial, stream),
-                "front");
-        TRY_HIP(muon::launch_norm(p, partial, inv, true, stream), "norm");
-        const muon::FusedApply fuse{params, param_dtype, h, copy};
-        TRY_HIP(muon::launch_newton_schulz(p, ws, u, &fuse, ns_steps, stream), "newton-schulz");
-    } else {
-        TRY_HIP(muon::launch_front(p, grads, momentum, u, partial, h, stream), "front");
-        TRY_HIP(muon::launch_norm(p, partial, inv, false, stream), "norm");
-        TRY_HIP(muon::launch_cast(p, u, inv, ws, u, stream), "cast");
-        TRY_HIP(muon::launch_apply(p, params, param_dtype, u, h, copy, stream), "apply");
-    }
+    std::shared_ptr<const muon::StepPlan> plan;
+    TRY(muon::get_plan(descs, n, gemm_mode, capacity, stream, &plan, &st));
+    std::vector<muon::PlanView> views;
+    for (int w = 0; w < muon::plan_waves(*plan); ++w) views.push_back(muon::wave_view(*plan, w));
+    TRY_HIP(muon::enqueue_step(views.data(), int(views.size()), params, param_dtype,
+                               static_cast<uint16_t*>(model_copy), grads, momentum, h, ns_steps,
+                               workspace, stream),
+            "step");
     return MUON_OK;
 }
 
 }  // namespace
+
+namespace muon {
+
+// The step's launches, wave after wave on one stream (each wave reuses the
+// whole workspace: stream order keeps the waves apart).
+hipError_t enqueue_step(const PlanView* views, int n_waves, void* params, int param_dtype,
+                        uint16_t* copy, const float* grads, float* momentum, const Hyper& h,
+                        int ns_steps, void* workspace, hipStream_t stream) {
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    for (int w = 0; w < n_waves; ++w) {
+        const PlanView& p = views[w];
+        float* u = reinterpret_cast<float*>(ws + p.ws.u);
+        float* partial = reinterpret_cast<float*>(ws + p.ws.partial);
+        float* inv = reinterpret_cast<float*>(ws + p.ws.inv);
+        hipError_t e;
+        if (ns_steps > 0) {
+            // momentum, input and first iterate in one pass; the norm is folded into
+            // iteration 0, and the last iteration applies the update itself (same
+            // roundings as the apply phase)
+            if ((e = launch_front_cast(p, grads, momentum, nullptr, h, ws, partial, stream)) != hipSuccess)
+                return e;
+            if ((e = launch_norm(p, partial, inv, true, stream)) != hipSuccess) return e;
+            const FusedApply fuse{params, param_dtype, h, copy};
+            if ((e = launch_newton_schulz(p, ws, nullptr, &fuse, ns_steps, stream)) != hipSuccess)
+                return e;
+        } else {
+            // U and O (in place) in the compact region over the unused X / A / B
+            if ((e = launch_front(p, grads, momentum, u, true, partial, h, stream)) != hipSuccess)
+                return e;
+            if ((e = launch_norm(p, partial, inv, false, stream)) != hipSuccess) return e;
+            if ((e = launch_cast(p, u, inv, ws, u, true, stream)) != hipSuccess) return e;
+            if ((e = launch_apply(p, params, param_dtype, u, true, h, copy, stream)) != hipSuccess)
+                return e;
+        }
+    }
+    return hipSuccess;
+}
+
+}  // namespace muon
 
 extern "C" {
 
@@ -178,6 +212,16 @@ int muon_workspace_bytes(const muon_matrix_desc_t* descs, int64_t n, int gemm_mo
     // any group index is fine here: the workspace does not depend on groups
     TRY(muon::check_desc_shapes(descs, n, &st, INT32_MAX));
     *out_bytes = muon::workspace_bytes_for(descs, n, gemm_mode);
+    return MUON_OK;
+}
+
+int muon_workspace_min_bytes(const muon_matrix_desc_t* descs, int64_t n, int gemm_mode,
+                             size_t* out_bytes) {
+    Status st{MUON_OK, ""};
+    TRY(check_null(out_bytes, "out_bytes", &st));
+    TRY(check_mode(gemm_mode, &st));
+    TRY(muon::check_desc_shapes(descs, n, &st, INT32_MAX));
+    *out_bytes = muon::min_workspace_bytes_for(descs, n, gemm_mode);
     return MUON_OK;
 }
 
@@ -230,11 +274,12 @@ int muon_momentum(const float* grads, float* momentum, float* u_out, int64_t n_s
                                    {momentum, size_t(n_state_elems) * 4, "momentum"},
                                    {u_out, size_t(n_state_elems) * 4, "u_out"}};
     TRY(muon::check_no_alias(ranges, 3, &st));
-    std::shared_ptr<const muon::PlanStore> plan;
-    TRY(muon::get_plan(descs, n, MUON_GEMM_BF16_MFMA, stream, &plan, &st));
-    const muon::PlanView& p = muon::view_of(*plan);
+    std::shared_ptr<const muon::StepPlan> plan;
+    TRY(muon::get_plan(descs, n, MUON_GEMM_BF16_MFMA, 0, stream, &plan, &st));
     const muon::Hyper h{nullptr, 0.f, 0.f, beta, nesterov};
-    TRY_HIP(muon::launch_front(p, grads, momentum, u_out, nullptr, h, stream), "front");
+    TRY_HIP(muon::launch_front(muon::wave_view(*plan, 0), grads, momentum, u_out, false, nullptr,
+                               h, stream),
+            "front");
     return MUON_OK;
 }
 
@@ -249,28 +294,33 @@ int muon_orthogonalize(const float* u, float* o_out, int64_t n_elems,
     TRY(check_null(u, "u", &st));
     TRY(check_null(o_out, "o_out", &st));
     TRY(muon::check_state_ranges(descs, n, n_elems, "u/o_out", &st));
-    const size_t need = muon::workspace_bytes_for(descs, n, gemm_mode);
-    TRY(check_workspace(workspace, workspace_bytes, need, &st));
+    size_t capacity = 0;
+    TRY(check_workspace(workspace, workspace_bytes, muon::workspace_bytes_for(descs, n, gemm_mode),
+                        muon::min_workspace_bytes_for(descs, n, gemm_mode), &capacity, &st));
     const bool in_place = static_cast<const void*>(u) == static_cast<const void*>(o_out);
     const muon::Range ranges[3] = {{u, size_t(n_elems) * 4, "u"},
                                    {o_out, in_place ? 0 : size_t(n_elems) * 4, "o_out"},
                                    {workspace, workspace_bytes, "workspace"}};
     TRY(muon::check_no_alias(ranges, 3, &st));
-    std::shared_ptr<const muon::PlanStore> plan;
-    TRY(muon::get_plan(descs, n, gemm_mode, stream, &plan, &st));
-    const muon::PlanView& p = muon::view_of(*plan);
+    std::shared_ptr<const muon::StepPlan> plan;
+    TRY(muon::get_plan(descs, n, gemm_mode, capacity, stream, &plan, &st));
     unsigned char* ws = static_cast<unsigned char*>(workspace);
-    float* partial = reinterpret_cast<float*>(ws + p.ws.partial);
-    float* inv = reinterpret_cast<float*>(ws + p.ws.inv);
-    if (ns_steps > 0) {
-        TRY_HIP(muon::launch_front_cast(p, nullptr, nullptr, u, muon::Hyper{}, ws, partial, stream),
-                "sum of squares and cast");
-        TRY_HIP(muon::launch_norm(p, partial, inv, true, stream), "norm");
-        TRY_HIP(muon::launch_newton_schulz(p, ws, o_out, nullptr, ns_steps, stream), "newton-schulz");
-    } else {
-        TRY_HIP(muon::launch_sumsq(p, u, partial, stream), "sum of squares");
-        TRY_HIP(muon::launch_norm(p, partial, inv, false, stream), "norm");
-        TRY_HIP(muon::launch_cast(p, u, inv, ws, o_out, stream), "cast");
+    for (int w = 0; w < muon::plan_waves(*plan); ++w) {
+        const muon::PlanView& p = muon::wave_view(*plan, w);
+        float* partial = reinterpret_cast<float*>(ws + p.ws.partial);
+        float* inv = reinterpret_cast<float*>(ws + p.ws.inv);
+        if (ns_steps > 0) {
+            TRY_HIP(muon::launch_front_cast(p, nullptr, nullptr, u, muon::Hyper{}, ws, partial,
+                                            stream),
+                    "sum of squares and cast");
+            TRY_HIP(muon::launch_norm(p, partial, inv, true, stream), "norm");
+            TRY_HIP(muon::launch_newton_schulz(p, ws, o_out, nullptr, ns_steps, stream),
+                    "newton-schulz");
+        } else {
+            TRY_HIP(muon::launch_sumsq(p, u, partial, stream), "sum of squares");
+            TRY_HIP(muon::launch_norm(p, partial, inv, false, stream), "norm");
+            TRY_HIP(muon::launch_cast(p, u, inv, ws, o_out, false, stream), "cast");
+        }
     }
     return MUON_OK;
 }
@@ -292,11 +342,11 @@ int muon_apply(void* params, int param_dtype, int64_t n_param_elems, const float
     const muon::Range ranges[2] = {{params, param_bytes(param_dtype, n_param_elems), "params"},
                                    {updates, size_t(n_update_elems) * 4, "updates"}};
     TRY(muon::check_no_alias(ranges, 2, &st));
-    std::shared_ptr<const muon::PlanStore> plan;
-    TRY(muon::get_plan(descs, n, MUON_GEMM_BF16_MFMA, stream, &plan, &st));
+    std::shared_ptr<const muon::StepPlan> plan;
+    TRY(muon::get_plan(descs, n, MUON_GEMM_BF16_MFMA, 0, stream, &plan, &st));
     const muon::Hyper h{nullptr, lr, weight_decay, 0.f, 0};
-    TRY_HIP(muon::launch_apply(muon::view_of(*plan), params, param_dtype, updates, h, nullptr,
-                               stream),
+    TRY_HIP(muon::launch_apply(muon::wave_view(*plan, 0), params, param_dtype, updates, false, h,
+                               nullptr, stream),
             "apply");
     return MUON_OK;
 }

@@ -59,6 +59,7 @@ struct alignas(16) MatInfo {
     int64_t slice_len;  // numel / n_shards
     int64_t x_off;      // start of X (rp x cp) in each of the two X regions
     int64_t g_off;      // start of the rp x rp Gram block in the A and B regions
+    int64_t u_off;      // start of the matrix's U / O in the workspace's compact float32 U region
     int32_t R, C;       // original shape
     int32_t r, c;       // NS-orientation shape
     int32_t rp, cp;     // padded NS-orientation shape
@@ -69,7 +70,6 @@ struct alignas(16) MatInfo {
     float scale;        // (float) sqrt(max(1, R/C))
     int32_t group;      // optimizer group (muon_step_grouped), else 0
     int32_t ns_f32;     // products, X, A and B in float32 (x_off, g_off count floats)
-    int32_t pad_;
 };
 static_assert(sizeof(MatInfo) == 128, "MatInfo layout");
 
@@ -78,9 +78,10 @@ struct alignas(16) GemmTile {
     int32_t mat, ti, tj, pad_;
 };
 
-// Byte offsets of the workspace regions.
+// Byte offsets of the workspace regions.  The compact U / O region is used only
+// by muon_step with ns_steps == 0, which uses no X, A or B: it overlays them.
 struct WsLayout {
-    size_t u;        // float32 U / O, laid out like grads (state extent E)
+    size_t u;        // float32 U / O, matrix i at MatInfo::u_off (compact, 256-byte aligned)
     size_t x[2];     // X ping-pong (iteration input / output), rp x cp per matrix
     size_t a, b;     // Gram matrices rp x rp per matrix
     size_t partial;  // one float per elementwise chunk
@@ -143,17 +144,38 @@ int check_scalar(float v, const char* name, Status* st);
 
 // --------------------------------------------------------------------- plan
 
-// Workspace bytes for a descriptor set (host only; shapes must be valid).
+// Workspace bytes for a descriptor set run in one wave (host only; shapes
+// must be valid).
 size_t workspace_bytes_for(const muon_matrix_desc_t* d, int64_t n, int gemm_mode);
+// Smallest workspace that runs the set at all: the largest one-matrix wave.
+size_t min_workspace_bytes_for(const muon_matrix_desc_t* d, int64_t n, int gemm_mode);
 
-// Owner of one plan's host tables and device memory.
-struct PlanStore;
-const PlanView& view_of(const PlanStore& s);
+// A launch plan: the descriptor set cut into waves whose workspace regions fit
+// a capacity (one wave when unbounded), each wave with its own tables.
+struct StepPlan;
+int plan_waves(const StepPlan& p);
+const PlanView& wave_view(const StepPlan& p, int wave);
 
-// Cached plan for (device, gemm_mode, descriptors); builds and uploads it on
-// first use.  The shared pointer keeps the plan alive for the caller.
-int get_plan(const muon_matrix_desc_t* d, int64_t n, int gemm_mode, hipStream_t stream,
-             std::shared_ptr<const PlanStore>* out, Status* st);
+// Cached plan for (device, gemm_mode, capacity, descriptors); builds and
+// uploads it on first use (outside graph capture).  capacity: workspace bytes
+// available, 0 = one wave.  A plan fetched while `stream` is being captured
+// is pinned (kept until the process ends).  The shared pointer keeps the plan
+// alive for the caller.
+int get_plan(const muon_matrix_desc_t* d, int64_t n, int gemm_mode, size_t capacity,
+             hipStream_t stream, std::shared_ptr<const StepPlan>* out, Status* st);
+
+// A plan built on the host only (no device memory): its tables as one blob
+// (blob_bytes), to be copied to a device address and bound there.  For callers
+// that cannot allocate; not cached.
+struct HostPlan;
+int build_host_plan(const muon_matrix_desc_t* d, int64_t n, int gemm_mode, size_t capacity,
+                    std::unique_ptr<HostPlan>* out, Status* st);
+size_t host_plan_blob_bytes(const HostPlan& p);
+const void* host_plan_blob(const HostPlan& p);
+size_t host_plan_workspace_bytes(const HostPlan& p);  // largest wave's workspace
+// Views of every wave with their tables at dev_blob (a device copy of the blob).
+int host_plan_waves(const HostPlan& p);
+PlanView host_plan_view(const HostPlan& p, int wave, const void* dev_blob);
 
 // ---------------------------------------------------------------- profiling
 
@@ -184,10 +206,12 @@ struct Hyper {
 };
 
 
-// Momentum + orthogonalization input (+ per-chunk sum of squares of U).
+// Momentum + orthogonalization input (+ per-chunk sum of squares of U).  U is
+// written at each matrix's offset in the grads layout, or (compact) at its
+// u_off in the workspace's U region.
 hipError_t launch_front(const PlanView& p, const float* grads, float* momentum, float* u,
-                        float* partial, const Hyper& h, hipStream_t s);
-// Per-chunk sum of squares of an existing U.
+                        bool compact, float* partial, const Hyper& h, hipStream_t s);
+// Per-chunk sum of squares of an existing U (grads layout).
 hipError_t launch_sumsq(const PlanView& p, const float* u, float* partial, hipStream_t s);
 // Per-matrix 1 / (sqrt(sum of partials) + eps); partials per elementwise chunk,
 // or per 64 x 64 cast tile (per_tile).
@@ -204,9 +228,9 @@ hipError_t launch_front_cast(const PlanView& p, const float* grads, float* momen
                              hipStream_t s);
 // X0 = cast(U * inv) in NS orientation into the first X region, zero
 // padding; when o_direct is non-null (ns_steps == 0) write O = s * X0 there
-// instead.
+// instead.  U and O in the grads layout, or both compact (u_off).
 hipError_t launch_cast(const PlanView& p, const float* u, const float* inv, void* ws,
-                       float* o_direct, hipStream_t s);
+                       float* o_direct, bool compact, hipStream_t s);
 // The decay-and-update of the apply phase, for the last Newton-Schulz
 // iteration to perform in place of storing O.  model_copy (float32 params
 // only, may be null) receives every updated weight rounded to bfloat16.
@@ -224,9 +248,16 @@ struct FusedApply {
 // stored).
 hipError_t launch_newton_schulz(const PlanView& p, void* ws, float* o, const FusedApply* fuse,
                                 int ns_steps, hipStream_t s);
+// The whole step (ns_steps >= 1: front_cast, norm, Newton-Schulz with the
+// fused apply; ns_steps == 0: front, norm, cast and apply through the compact U
+// region), wave after wave on one stream, every wave reusing the workspace.
+hipError_t enqueue_step(const PlanView* views, int n_waves, void* params, int param_dtype,
+                        uint16_t* copy, const float* grads, float* momentum, const Hyper& h,
+                        int ns_steps, void* workspace, hipStream_t stream);
 // W <- fl(fl(W*f) - fl(lr*O)) scattered into the slices (and, with
-// model_copy, its bfloat16 rounding into the copy).
+// model_copy, its bfloat16 rounding into the copy).  O in the grads layout, or
+// compact (u_off).
 hipError_t launch_apply(const PlanView& p, void* params, int param_dtype, const float* o,
-                        const Hyper& h, uint16_t* model_copy, hipStream_t s);
+                        bool compact, const Hyper& h, uint16_t* model_copy, hipStream_t s);
 
 }  // namespace muon

@@ -65,14 +65,37 @@ def test_workspace_bytes_sizes(lib):
     assert rc == 0 and zero == 0
     rc, a = ws_bytes(lib, [(0, 256, 512)])
     assert rc == 0 and a % 256 == 0
-    # U/O region (4 B x 131072) + two X iterates (bf16, 256 x 512 each) + A, B (256 x 256)
-    assert a >= 4 * 131072 + 2 * 2 * 256 * 512 + 2 * 2 * 256 * 256
+    # two X iterates (bf16, 256 x 512 each) + A, B (256 x 256); the float32 U/O
+    # region of ns_steps == 0 (4 B x 131072) overlays them
+    assert a >= 2 * 2 * 256 * 512 + 2 * 2 * 256 * 256
+    assert a < 4 * 131072 + 2 * 2 * 256 * 512 + 2 * 2 * 256 * 256
     rc, f = ws_bytes(lib, [(0, 256, 512)], mode=1)
     assert rc == 0 and f > a  # float32 intermediates are larger
     rc, two = ws_bytes(lib, [(0, 256, 512), (131072, 300, 17)])
     assert rc == 0 and two > a
     # the transposed shape needs the same intermediates
     assert ws_bytes(lib, [(0, 512, 256)])[1] == a
+
+
+def ws_min_bytes(lib, items, mode=0):
+    arr, n = descs(*items)
+    out = ctypes.c_size_t(0)
+    rc = lib.muon_workspace_min_bytes(arr, n, mode, ctypes.byref(out))
+    return rc, out.value
+
+
+def test_workspace_min_bytes(lib):
+    one = [(0, 1024, 4096)]
+    assert ws_min_bytes(lib, one) == ws_bytes(lib, one)  # one matrix: one wave either way
+    many = [(k * 4096 * 1024, 1024, 4096) for k in range(6)] + [(6 * 4096 * 1024, 300, 17)]
+    rc, lo = ws_min_bytes(lib, many)
+    rc2, hi = ws_bytes(lib, many)
+    assert rc == 0 and rc2 == 0 and lo < hi
+    assert lo == ws_bytes(lib, [many[0]])[1]  # the largest single matrix
+    assert ws_min_bytes(lib, [])[1] == 0
+    arr, n = descs((0, 4, 4))
+    assert lib.muon_workspace_min_bytes(arr, n, 0, None) == ERR["NULL_POINTER"]
+    assert lib.muon_workspace_min_bytes(arr, n, 5, ctypes.byref(ctypes.c_size_t())) == ERR["BAD_ARG"]
 
 
 @pytest.mark.parametrize("item,code", [
@@ -246,3 +269,12 @@ def test_grouped_accepts_groups_in_workspace_sizing(lib):
 def test_grouped_no_matrices_is_a_noop(lib):
     assert grouped(lib, [], params=None, grads=None, momentum=None, groups=None, ws=None,
                    ws_size=0) == 0
+
+
+def test_default_workspace_refused_under_capture(monkeypatch):
+    """The default workspace cache cannot serve a call made under graph capture
+    (a later, larger set could free it while the graph still points at it)."""
+    import torch
+    monkeypatch.setattr(torch.cuda, "is_current_stream_capturing", lambda: True)
+    with pytest.raises(RuntimeError, match="explicit workspace"):
+        nsf.workspace_for([(0, 8, 8)], "bf16", "cuda:0")

@@ -4,14 +4,16 @@ properties that hold at any size.
 * llama layer (the benchmarked workload, in the benchmark's launch
   configuration): the whole step equals its phase composition bit for bit;
   momentum and Nesterov input bit for bit for all 218 M elements; O of Wk, Wv,
-  Wq against the fp64 oracle; for every matrix, two size-independent
-  properties of the exact iteration:
+  Wq, gate (tall) and down (K = 14336) -- every distinct shape -- against the
+  fp64 oracle; for every matrix, two size-independent properties of the exact
+  iteration:
     - trace identity: ||O||_F^2 / s^2 = sum_i f^5(sigma_i)^2, with sigma_i the
       singular values of the normalized input (eigenvalues of U U^T, float64);
     - symmetry: (O/s) X0^T is symmetric, because every iterate is a
       polynomial in X0 X0^T times X0.
-* MoE set and the 224-matrix owner share: sampled matrices orthogonalized on
-  their own (grouping invariance) match the oracle, and the full step's
+* MoE set and the 224-matrix owner share: sampled matrices (including the
+  7168 x 18432 dense matrix) orthogonalized on their own (grouping invariance)
+  match the oracle, and the full step's
   weights for those matrices equal the same-order apply of that O bit for bit,
   across all 8 shard slices.
 """
@@ -87,7 +89,9 @@ def test_llama_layer_full_size(nsf, torch):
         want_m, want_u = so.front(mat(gh, d), mat(m0, d), H["beta"], True)
         assert np.array_equal(bits(mat(mh, d)), bits(want_m))
         assert np.array_equal(bits(mat(uh, d)), bits(want_u))
-    for name in ("wk", "wv", "wq"):
+    # every distinct shape against the fp64 oracle element by element: 1024 x 4096,
+    # 4096 x 4096, 14336 x 4096 (tall, scale sqrt(3.5)) and 4096 x 14336 (K = 14336)
+    for name in ("wk", "wv", "wq", "gate", "down"):
         d = wl.descs[wl.names.index(name)]
         err = rel_fro(mat(oh, d), mo.newton_schulz(mat(uh, d).astype(np.float64), 5))
         say("llama oracle", name, err)
@@ -154,7 +158,7 @@ def _sampled_check(nsf, torch, wl, oracle_names, property_names=(), mode="bf16")
 
 def test_moe_set_sampled(nsf, torch):
     wl = wlm.make_workload("moe")
-    _sampled_check(nsf, torch, wl, ["expert_up0", "expert_down63"], ["dense_up", "dense_down"])
+    _sampled_check(nsf, torch, wl, ["expert_up0", "expert_down63", "dense_up"], ["dense_down"])
 
 
 def test_owner_share_sampled(nsf, torch):

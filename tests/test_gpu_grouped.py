@@ -8,7 +8,8 @@ device table, the optional bfloat16 model copy, and HIP-graph capture).
 * The model copy is the round-to-nearest-even bfloat16 of the updated
   float32 weights, bit for bit.
 * A captured graph replayed with different group values between replays
-  matches the same sequence of eager calls after every replay.
+  matches the same sequence of eager calls after every replay, and the fp64
+  oracle and same-order chain with that replay's groups.
 """
 
 import dataclasses
@@ -137,38 +138,72 @@ def test_model_copy_is_rounded_weights(nsf, torch, mode, ns_steps):
     assert not np.any(c[~covered])
 
 
+def _check_against_oracle(descs, rows, w_before, m_before, gh, w_after, m_after, mode):
+    """M bit for bit against the same-order chain; W_before - W_after against
+    the fp64 oracle with each matrix's group (float32 weights)."""
+    for d in descs:
+        lr, wd, beta, nest = rows[d.group]
+        want_m, want_u = so.front(mat(gh, d), mat(m_before, d), beta, nest)
+        assert np.array_equal(bits(mat(m_after, d)), bits(want_m)), d
+        o = mo.newton_schulz(want_u.astype(np.float64), H["ns_steps"])
+        lr64, wd64 = mo.as_f32_value(lr), mo.as_f32_value(wd)
+        wb = param_slices(w_before, d).astype(np.float64).reshape(d.rows, d.cols)
+        delta_want = wb * (lr64 * wd64) + lr64 * o
+        delta_got = wb - param_slices(w_after, d).astype(np.float64).reshape(d.rows, d.cols)
+        assert rel_fro(delta_got, delta_want) <= TOL[mode] + 1e-4, d
+
+
 def test_graph_capture_replays_follow_the_table(nsf, torch):
-    """Capture one grouped step in a HIP graph; replay it three times, changing
-    the device group table between replays (eager work, with synchronization,
-    outside the graph), and compare every replay with the same eager call."""
-    wl = wlm.small_mixed(35, count=6, max_side=300, param_dtype="bf16", shards=2)
+    """Capture one grouped step (float32 master weights, bfloat16 model copy,
+    slices in two shards) in a HIP graph; replay it three times, changing the
+    device group table between replays (eager work, with synchronization,
+    outside the graph).  After every replay: the same eager call bit for bit,
+    M bit for bit against the same-order chain, the weight change against the
+    fp64 oracle, and the model copy equal to the rounded weights."""
+    wl = wlm.small_mixed(35, count=6, max_side=300, param_dtype="f32", shards=2)
     descs = with_groups(wl.descs, 2)
+    mode = "bf16"
     say("graph capture", wl.name)
     params, grads, mom = wlm.make_tensors(wl, "cuda", momentum_std=1e-3)
     pe, me = params.clone(), mom.clone()
+    copy = torch.zeros(params.numel(), dtype=torch.bfloat16, device="cuda")
+    copy_e = torch.zeros_like(copy)
     table = nsf.group_table(GROUPS[:2], "cuda")
     eager_table = table.clone()
-    ws = torch.empty(nsf.muon_workspace_bytes(descs, "bf16"), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(nsf.muon_workspace_bytes(descs, mode), dtype=torch.uint8, device="cuda")
     ws_e = torch.empty_like(ws)
     # first call (plan build) outside capture, on throwaway copies
-    nsf.muon_step_grouped(params.clone(), grads, mom.clone(), descs, table, workspace=ws)
+    nsf.muon_step_grouped(params.clone(), grads, mom.clone(), descs, table, workspace=ws,
+                          model_copy=copy.clone())
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         with torch.cuda.graph(graph):
-            nsf.muon_step_grouped(params, grads, mom, descs, table, workspace=ws)
+            nsf.muon_step_grouped(params, grads, mom, descs, table, workspace=ws,
+                                  model_copy=copy)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
+    gh = host(grads)
     schedules = [GROUPS[:2], [GROUPS[2], GROUPS[1]], [(0.01, 0.05, 0.5, False), GROUPS[0]]]
     for rep, rows in enumerate(schedules):
         new = nsf.group_table(rows, "cuda")
         table.copy_(new)
         eager_table.copy_(new)
         torch.cuda.synchronize()
+        w_before, m_before = host(params), host(mom)
         graph.replay()
-        nsf.muon_step_grouped(pe, grads, me, descs, eager_table, workspace=ws_e)
+        nsf.muon_step_grouped(pe, grads, me, descs, eager_table, workspace=ws_e,
+                              model_copy=copy_e)
         torch.cuda.synchronize()
-        assert np.array_equal(bits(host(params)), bits(host(pe))), rep
-        assert np.array_equal(bits(host(mom)), bits(host(me))), rep
+        w_after, m_after = host(params), host(mom)
+        say("graph replay", rep, rows)
+        assert np.array_equal(bits(w_after), bits(host(pe))), rep
+        assert np.array_equal(bits(m_after), bits(host(me))), rep
+        assert np.array_equal(host(copy), host(copy_e)), rep
+        _check_against_oracle(descs, rows, w_before, m_before, gh, w_after, m_after, mode)
+        c = host(copy)
+        for d in descs:
+            assert np.array_equal(param_slices(c, d),
+                                  so.f32_to_bf16_bits(param_slices(w_after, d))), (rep, d)

@@ -150,17 +150,21 @@ def test_many_tiny_matrices(nsf, torch, mode):
     assert np.all(oh[~cov] == 3.0)
 
 
-@pytest.mark.parametrize("rank", [1, 8])
-def test_rank_deficient_float32(nsf, torch, rank):
+@pytest.mark.parametrize("mode", ["f32", "bf16"])
+@pytest.mark.parametrize("rank", [1, 8, 64])
+def test_rank_deficient(nsf, torch, rank, mode):
     """Rank-deficient inputs U = P Q (P 1024 x rank, Q rank x 1024; 256 x rank,
-    rank x 512), float32 mode.  The exact O lives in U's column and row spaces;
-    what the iteration does with U's null space is not unique in finite
-    precision: each step multiplies a perturbation there by f'(0) = a, so
-    rounding noise of relative size e (float32 products over K terms: about
-    sqrt(K) 2^-24) grows to about a^5 e.  Checked: the projection of O onto U's
-    column and row spaces against the fp64 oracle within the float32 tolerance,
-    and the rest of O within a^5 sqrt(K) 2^-24 of ||O||."""
-    say("rank deficient float32", rank)
+    rank x 512).  The exact O lives in U's column and row spaces; what the
+    iteration does with U's null space is not unique in finite precision: each
+    step multiplies a perturbation there by f'(0) = a, so rounding noise of
+    relative size e (float32 products over K terms: about sqrt(K) 2^-24) grows
+    to about a^5 e.  Checked: the projection of O onto U's column and row spaces
+    against the fp64 oracle within the mode's tolerance; in float32 also the
+    rest of O within a^5 sqrt(K) 2^-24 of ||O||.  With bfloat16 iterates the
+    rest reaches the order of ||O|| (a property of the bfloat16 iteration: a
+    CPU emulation gives 118% at rank 1, 15-35% at ranks 8-64), so only its
+    size is reported."""
+    say("rank deficient", mode, rank)
     shapes = [(1024, 1024), (256, 512)]
     descs, off = [], 0
     for r, c in shapes:
@@ -173,7 +177,7 @@ def test_rank_deficient_float32(nsf, torch, rank):
         q = torch.randn(rank, d.cols, device="cuda", generator=g)
         u[d.offset:d.offset + d.rows * d.cols] = (p @ q).reshape(-1) * 1e-3
     o = torch.zeros_like(u)
-    nsf.muon_orthogonalize(u, o, descs, mode="f32")
+    nsf.muon_orthogonalize(u, o, descs, mode=mode)
     gpu_sync(torch)
     uh, oh = host(u), host(o)
     a5 = 3.4445 ** 5
@@ -192,10 +196,12 @@ def test_rank_deficient_float32(nsf, torch, rank):
         err_range = rel_fro(in_range, project(want))
         rest = np.linalg.norm(got - in_range) / np.linalg.norm(want)
         bound = a5 * np.sqrt(max(d.rows, d.cols)) * 2.0 ** -24  # K of the Gram product
-        say("rank", rank, (d.rows, d.cols), "k", k, "range", err_range, "rest", rest, "bound", bound)
+        say("rank", mode, rank, (d.rows, d.cols), "k", k, "range", err_range, "rest", rest,
+            "bound", bound)
         assert k == rank
-        assert err_range <= TOL["f32"], (rank, d.rows, d.cols, err_range)
-        assert rest <= bound, (rank, d.rows, d.cols, rest, bound)
+        assert err_range <= TOL[mode], (rank, d.rows, d.cols, err_range)
+        if mode == "f32":
+            assert rest <= bound, (rank, d.rows, d.cols, rest, bound)
 
 
 def test_orthogonalize_long_float32_contraction(nsf, torch):
