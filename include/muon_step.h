@@ -242,6 +242,26 @@ int muon_apply(void* params, int param_dtype, int64_t n_param_elems, const float
                int64_t n_update_elems, const muon_matrix_desc_t* descs, int64_t n, float lr,
                float weight_decay, hipStream_t stream);
 
+/* muon_step for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments and results (bit for bit) as muon_step, without the workspace:
+ * every intermediate lives in a fixed device array of 320 MiB that the library
+ * holds on each GPU it runs on, from its load until the process ends (8 MiB of
+ * launch tables, 312 MiB of workspace; matrices that do not fit at once run in
+ * waves).  The call makes no hipMalloc, hipFree or other allocation.  A matrix
+ * whose intermediates alone exceed 312 MiB (for example 4096 x 16384 with
+ * bfloat16 products), or a set whose launch tables exceed 8 MiB, is rejected
+ * with MUON_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.  The first
+ * call with a new descriptor set on a device copies its launch tables into the
+ * array and synchronizes `stream`; later calls with the same set copy nothing
+ * and do not synchronize.  All calls on one GPU share its array, which keeps
+ * the last call's contents: calls that overlap on one GPU (different streams,
+ * or threads without ordering) race and must not be made. */
+int muon_step_noalloc(void* params, int param_dtype, int64_t n_param_elems, const float* grads,
+                      float* momentum, int64_t n_state_elems, const muon_matrix_desc_t* descs,
+                      int64_t n, float lr, float weight_decay, float beta, int nesterov,
+                      int ns_steps, int gemm_mode, hipStream_t stream);
+
 /* Kernel timing, a profiling aid (not part of the step's semantics).
  * Between muon_profile_begin() and muon_profile_end(), every kernel the
  * library launches, from any thread, is bracketed by two HIP events recorded

@@ -9,6 +9,7 @@ fallback.
 Entry points (same names as the C ABI):
 
 ``muon_step``           momentum, Nesterov input, Newton-Schulz, decay + apply
+``muon_step_noalloc``   ``muon_step`` without workspace or device allocation
 ``muon_step_grouped``   the same with per-matrix optimizer groups read from a
                         device table (graph-capturable) and an optional
                         bfloat16 copy of float32 weights
@@ -40,9 +41,9 @@ MUON_GEMM_F32 = 1
 _MODES = {"bf16": MUON_GEMM_BF16_MFMA, "f32": MUON_GEMM_F32}
 
 #: C names of every exported entry point (mirrors include/muon_step.h).
-EXPORTS = ("muon_workspace_bytes", "muon_workspace_min_bytes", "muon_step", "muon_step_grouped", "muon_momentum",
-           "muon_orthogonalize", "muon_apply", "muon_profile_begin", "muon_profile_end",
-           "muon_status_string", "muon_last_error")
+EXPORTS = ("muon_workspace_bytes", "muon_workspace_min_bytes", "muon_step", "muon_step_grouped",
+           "muon_step_noalloc", "muon_momentum", "muon_orthogonalize", "muon_apply",
+           "muon_profile_begin", "muon_profile_end", "muon_status_string", "muon_last_error")
 
 
 class MatrixDescC(ctypes.Structure):
@@ -90,6 +91,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                               sz, p]
     lib.muon_step_grouped.argtypes = [p, i32, i64, p, p, p, i64, dp, i64, p, ctypes.c_int32, i32,
                                       i32, p, sz, p]
+    lib.muon_step_noalloc.argtypes = [p, i32, i64, p, p, i64, dp, i64, f32, f32, f32, i32, i32,
+                                      i32, p]
     lib.muon_momentum.argtypes = [p, p, p, i64, dp, i64, f32, i32, p]
     lib.muon_orthogonalize.argtypes = [p, p, i64, dp, i64, i32, i32, p, sz, p]
     lib.muon_apply.argtypes = [p, i32, i64, p, i64, dp, i64, f32, f32, p]
@@ -99,8 +102,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.muon_status_string.restype = ctypes.c_char_p
     lib.muon_last_error.argtypes = []
     lib.muon_last_error.restype = ctypes.c_char_p
-    for name in ("muon_workspace_bytes", "muon_workspace_min_bytes", "muon_step", "muon_step_grouped", "muon_momentum",
-                 "muon_orthogonalize", "muon_apply", "muon_profile_begin", "muon_profile_end"):
+    for name in ("muon_workspace_bytes", "muon_workspace_min_bytes", "muon_step",
+                 "muon_step_grouped", "muon_step_noalloc", "muon_momentum", "muon_orthogonalize",
+                 "muon_apply", "muon_profile_begin", "muon_profile_end"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -228,6 +232,23 @@ def muon_step(params, grads, momentum, descs, lr: float, weight_decay: float, be
                         lr, weight_decay, beta, int(bool(nesterov)), int(ns_steps), _mode(mode),
                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                         _stream(grads)))
+
+
+def muon_step_noalloc(params, grads, momentum, descs, lr: float, weight_decay: float,
+                      beta: float, nesterov: bool = True, ns_steps: int = 5, mode: str = "bf16"):
+    """``muon_step`` without a workspace and without any device allocation:
+    the library's fixed per-GPU scratch array holds every intermediate.  Calls
+    that overlap on one GPU race (they share the array)."""
+    import torch
+    _require(params, "params", (torch.float32, torch.bfloat16))
+    _require(grads, "grads", (torch.float32,))
+    _require(momentum, "momentum", (torch.float32,))
+    lib = load_library()
+    dt = MUON_DTYPE_BF16 if params.dtype == torch.bfloat16 else MUON_DTYPE_F32
+    check(lib.muon_step_noalloc(params.data_ptr(), dt, params.numel(), grads.data_ptr(),
+                                momentum.data_ptr(), grads.numel(), descs_array(descs),
+                                _count(descs), lr, weight_decay, beta, int(bool(nesterov)),
+                                int(ns_steps), _mode(mode), _stream(grads)))
 
 
 def group_table(groups, device):

@@ -29,6 +29,7 @@ SOURCES = [
     "k_elementwise.hip",
     "k_norm_cast.hip",
     "k_ns_gemm.hip",
+    "muon_noalloc.hip",
 ]
 # Sources whose arithmetic must round every operation separately.
 NO_CONTRACT = {"k_elementwise.hip", "k_norm_cast.hip"}

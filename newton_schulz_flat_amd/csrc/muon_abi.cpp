@@ -108,48 +108,82 @@ int check_workspace(const void* ws, size_t have, size_t need_full, size_t need_m
         if (e_ != hipSuccess) return finish((hip_fail(&st, e_, what), st)); \
     } while (0)
 
-// The whole step for muon_step and muon_step_grouped: validation of everything
-// but the scalars, then the launches.  h holds the scalars or the device group
-// array (n_groups groups).
+}  // namespace
+
+namespace muon {
+
+// Validation of a whole step's arguments except the workspace: descriptors,
+// mode, ns_steps, dtype, model copy, buffer bounds, alignment and aliasing of
+// the caller's buffers (and of `extra`, when given).  h holds the scalars or
+// the device group array (n_groups groups).
+int check_step_args(Status& st, void* params, int param_dtype, int64_t n_param_elems,
+                    void* model_copy, const float* grads, float* momentum, int64_t n_state_elems,
+                    const muon_matrix_desc_t* descs, int64_t n, const Hyper& h, int32_t n_groups,
+                    int ns_steps, int gemm_mode, const Range* extra) {
+    if (check_desc_shapes(descs, n, &st, n_groups) != MUON_OK) return st.code;
+    if (check_mode(gemm_mode, &st) != MUON_OK) return st.code;
+    if (check_ns_steps(ns_steps, &st) != MUON_OK) return st.code;
+    if (param_dtype != MUON_DTYPE_F32 && param_dtype != MUON_DTYPE_BF16 &&
+        check_param_ranges(descs, 0, 0, param_dtype, &st) != MUON_OK)
+        return st.code;
+    if (model_copy != nullptr && param_dtype != MUON_DTYPE_F32) {
+        st.code = MUON_ERR_BAD_ARG;
+        snprintf(st.msg, sizeof(st.msg), "model_copy needs float32 params (param_dtype %d)",
+                 param_dtype);
+        return st.code;
+    }
+    if (n == 0) return MUON_OK;
+    if (check_null(params, "params", &st) != MUON_OK) return st.code;
+    if (check_null(grads, "grads", &st) != MUON_OK) return st.code;
+    if (check_null(momentum, "momentum", &st) != MUON_OK) return st.code;
+    if (check_state_ranges(descs, n, n_state_elems, "grads/momentum", &st) != MUON_OK)
+        return st.code;
+    if (check_param_ranges(descs, n, n_param_elems, param_dtype, &st) != MUON_OK) return st.code;
+    if (model_copy != nullptr && reinterpret_cast<uintptr_t>(model_copy) % 16 != 0) {
+        st.code = MUON_ERR_MISALIGNED;
+        snprintf(st.msg, sizeof(st.msg), "model_copy is not 16-byte aligned");
+        return st.code;
+    }
+    const Range ranges[6] = {
+        {params, param_bytes(param_dtype, n_param_elems), "params"},
+        {grads, size_t(n_state_elems) * 4, "grads"},
+        {momentum, size_t(n_state_elems) * 4, "momentum"},
+        {h.groups, h.groups ? size_t(n_groups) * sizeof(muon_group_t) : 0, "groups"},
+        {model_copy, model_copy ? size_t(n_param_elems) * 2 : 0, "model_copy"},
+        extra ? *extra : Range{nullptr, 0, "unused"}};
+    return check_no_alias(ranges, 6, &st);
+}
+
+int check_step_scalars(Status& st, float lr, float weight_decay, float beta, int nesterov) {
+    if (check_flag(nesterov, "nesterov", &st) != MUON_OK) return st.code;
+    if (check_scalar(lr, "lr", &st) != MUON_OK) return st.code;
+    if (check_scalar(weight_decay, "weight_decay", &st) != MUON_OK) return st.code;
+    return check_scalar(beta, "beta", &st);
+}
+
+int report(const Status& st) { return finish(st); }
+
+int report_hip(Status& st, hipError_t e, const char* what) { return finish((hip_fail(&st, e, what), st)); }
+
+}  // namespace muon
+
+namespace {
+
+// The whole step for muon_step and muon_step_grouped: validation, then the
+// launches, in waves when the workspace is smaller than the one-wave size.
 int run_step(Status& st, void* params, int param_dtype, int64_t n_param_elems, void* model_copy,
              const float* grads, float* momentum, int64_t n_state_elems,
              const muon_matrix_desc_t* descs, int64_t n, const muon::Hyper& h, int32_t n_groups,
              int ns_steps, int gemm_mode, void* workspace, size_t workspace_bytes,
              hipStream_t stream) {
-    TRY(muon::check_desc_shapes(descs, n, &st, n_groups));
-    TRY(check_mode(gemm_mode, &st));
-    TRY(check_ns_steps(ns_steps, &st));
-    if (param_dtype != MUON_DTYPE_F32 && param_dtype != MUON_DTYPE_BF16)
-        TRY(muon::check_param_ranges(descs, 0, 0, param_dtype, &st));
-    if (model_copy != nullptr && param_dtype != MUON_DTYPE_F32) {
-        st.code = MUON_ERR_BAD_ARG;
-        snprintf(st.msg, sizeof(st.msg), "model_copy needs float32 params (param_dtype %d)",
-                 param_dtype);
-        return finish(st);
-    }
+    const muon::Range ws_range{workspace, workspace_bytes, "workspace"};
+    TRY(muon::check_step_args(st, params, param_dtype, n_param_elems, model_copy, grads,
+                              momentum, n_state_elems, descs, n, h, n_groups, ns_steps, gemm_mode,
+                              &ws_range));
     if (n == 0) return MUON_OK;
-    TRY(check_null(params, "params", &st));
-    TRY(check_null(grads, "grads", &st));
-    TRY(check_null(momentum, "momentum", &st));
-    TRY(muon::check_state_ranges(descs, n, n_state_elems, "grads/momentum", &st));
-    TRY(muon::check_param_ranges(descs, n, n_param_elems, param_dtype, &st));
-    if (model_copy != nullptr && reinterpret_cast<uintptr_t>(model_copy) % 16 != 0) {
-        st.code = MUON_ERR_MISALIGNED;
-        snprintf(st.msg, sizeof(st.msg), "model_copy is not 16-byte aligned");
-        return finish(st);
-    }
     size_t capacity = 0;
     TRY(check_workspace(workspace, workspace_bytes, muon::workspace_bytes_for(descs, n, gemm_mode),
                         muon::min_workspace_bytes_for(descs, n, gemm_mode), &capacity, &st));
-    const muon::Range ranges[6] = {
-        {params, param_bytes(param_dtype, n_param_elems), "params"},
-        {grads, size_t(n_state_elems) * 4, "grads"},
-        {momentum, size_t(n_state_elems) * 4, "momentum"},
-        {workspace, workspace_bytes, "workspace"},
-        {h.groups, h.groups ? size_t(n_groups) * sizeof(muon_group_t) : 0, "groups"},
-        {model_copy, model_copy ? size_t(n_param_elems) * 2 : 0, "model_copy"}};
-    TRY(muon::check_no_alias(ranges, 6, &st));
-
     std::shared_ptr<const muon::StepPlan> plan;
     TRY(muon::get_plan(descs, n, gemm_mode, capacity, stream, &plan, &st));
     std::vector<muon::PlanView> views;
@@ -230,10 +264,7 @@ int muon_step(void* params, int param_dtype, int64_t n_param_elems, const float*
               float lr, float weight_decay, float beta, int nesterov, int ns_steps, int gemm_mode,
               void* workspace, size_t workspace_bytes, hipStream_t stream) {
     Status st{MUON_OK, ""};
-    TRY(check_flag(nesterov, "nesterov", &st));
-    TRY(muon::check_scalar(lr, "lr", &st));
-    TRY(muon::check_scalar(weight_decay, "weight_decay", &st));
-    TRY(muon::check_scalar(beta, "beta", &st));
+    TRY(muon::check_step_scalars(st, lr, weight_decay, beta, nesterov));
     const muon::Hyper h{nullptr, lr, weight_decay, beta, nesterov};
     return run_step(st, params, param_dtype, n_param_elems, nullptr, grads, momentum, n_state_elems,
                     descs, n, h, 1, ns_steps, gemm_mode, workspace, workspace_bytes, stream);

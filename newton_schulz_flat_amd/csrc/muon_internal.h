@@ -142,6 +142,21 @@ struct Range {
 int check_no_alias(const Range* r, int count, Status* st);
 int check_scalar(float v, const char* name, Status* st);
 
+// Everything about a whole step's arguments except the workspace (shapes, mode,
+// ns_steps, dtype, model copy, bounds, alignment, aliasing -- also against
+// `extra` when non-null); h.groups and n_groups describe muon_step_grouped's
+// table.  The scalars of muon_step: nesterov in {0, 1}, finite lr, wd, beta.
+struct Hyper;
+int check_step_args(Status& st, void* params, int param_dtype, int64_t n_param_elems,
+                    void* model_copy, const float* grads, float* momentum, int64_t n_state_elems,
+                    const muon_matrix_desc_t* descs, int64_t n, const Hyper& h, int32_t n_groups,
+                    int ns_steps, int gemm_mode, const Range* extra);
+int check_step_scalars(Status& st, float lr, float weight_decay, float beta, int nesterov);
+// Records a failure as the calling thread's last error (muon_last_error);
+// returns its code.  report_hip fills st from a HIP error first.
+int report(const Status& st);
+int report_hip(Status& st, hipError_t e, const char* what);
+
 // --------------------------------------------------------------------- plan
 
 // Workspace bytes for a descriptor set run in one wave (host only; shapes
@@ -169,7 +184,7 @@ int get_plan(const muon_matrix_desc_t* d, int64_t n, int gemm_mode, size_t capac
 // that cannot allocate; not cached.
 struct HostPlan;
 int build_host_plan(const muon_matrix_desc_t* d, int64_t n, int gemm_mode, size_t capacity,
-                    std::unique_ptr<HostPlan>* out, Status* st);
+                    std::shared_ptr<HostPlan>* out, Status* st);
 size_t host_plan_blob_bytes(const HostPlan& p);
 const void* host_plan_blob(const HostPlan& p);
 size_t host_plan_workspace_bytes(const HostPlan& p);  // largest wave's workspace

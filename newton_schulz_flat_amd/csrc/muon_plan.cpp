@@ -544,9 +544,9 @@ int get_plan(const muon_matrix_desc_t* d, int64_t n, int gemm_mode, size_t capac
 }
 
 int build_host_plan(const muon_matrix_desc_t* d, int64_t n, int gemm_mode, size_t capacity,
-                    std::unique_ptr<HostPlan>* out, Status* st) {
+                    std::shared_ptr<HostPlan>* out, Status* st) {
     (void)st;
-    auto p = std::make_unique<HostPlan>();
+    auto p = std::make_shared<HostPlan>();
     p->gemm_mode = gemm_mode;
     p->waves = build_waves(d, n, gemm_mode, capacity);
     pack_waves(p->waves, &p->at, &p->blob);
