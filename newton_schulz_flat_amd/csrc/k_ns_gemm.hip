@@ -70,6 +70,7 @@ struct NsArgs {
     Hyper hyper;
     uint16_t* model_copy;
     int fuse, param_bf16;
+    int split;  // mixed launches: table slots below split are 128-tiles, the rest 64-tiles
 };
 
 constexpr int kRowBytes = 128;  // K block: bytes of one operand row
@@ -368,31 +369,44 @@ __device__ __forceinline__ void store_q(unsigned char* dst, const u32x4 (&pb)[kL
     }
 }
 
+// LDS layout of one tile size, type and stage: double-buffered operand tiles.
+// How stage X stages its Q = X^T; every other operand is a copy of rows.
+//  bf16: K rows of X are copied as they are (an LDS row of kS bytes holds the
+//        tile's TILE columns of one K row) and the fragment reads transpose
+//        them with ds_read_b64_tr_b16;
+//  f32:  blocks of X are transposed in registers on their way into LDS.
 template <int TILE, bool BF16, int STAGE>
-__global__ __launch_bounds__((Geo<TILE, BF16>::kThreads), (Geo<TILE, BF16>::kMinWaves)) void ns_gemm_kernel(
-    NsArgs args) {
-    using TE = std::conditional_t<BF16, uint16_t, float>;
+struct Lds {
     using G = Geo<TILE, BF16>;
-    constexpr int kEs = BF16 ? 2 : 4;
-    constexpr int kBk = kRowBytes / kEs;  // K elements per block
-    constexpr int kMi = G::kMi, kNj = G::kNj;
-    constexpr int kL = G::kLoads;
-    // How stage X stages its Q = X^T; every other operand is a copy of rows.
-    //  bf16: K rows of X are copied as they are (an LDS row of kS bytes holds the
-    //        tile's TILE columns of one K row) and the fragment reads transpose
-    //        them with ds_read_b64_tr_b16;
-    //  f32:  blocks of X are transposed in registers on their way into LDS.
-    constexpr bool kQLdsT = STAGE == kStageX && BF16;
-    constexpr bool kTransQ = STAGE == kStageX && !BF16;
+    static constexpr int kEs = BF16 ? 2 : 4;
+    static constexpr int kBk = kRowBytes / kEs;  // K elements per block
+    static constexpr bool kQLdsT = STAGE == kStageX && BF16;
+    static constexpr bool kTransQ = STAGE == kStageX && !BF16;
     // kS = 64 (mod 256) bytes: the four K rows one transposing read gathers
     // start in distinct quarters of the 256-byte bank space
-    constexpr int kS = TILE * 2 + 64;
-    constexpr int kOpQ = (kQLdsT && kBk * kS > G::kOp) ? kBk * kS : G::kOp;
-    constexpr int kBuf = G::kOp + kOpQ;  // one stage of the double-buffered operands
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kBuf];
+    static constexpr int kS = TILE * 2 + 64;
+    static constexpr int kOpQ = (kQLdsT && kBk * kS > G::kOp) ? kBk * kS : G::kOp;
+    static constexpr int kBuf = G::kOp + kOpQ;  // one stage of the double-buffered operands
+    static constexpr int kBytes = 2 * kBuf;
+};
 
-    const GemmTile tile = args.tiles[blockIdx.x];
-    if (tile.mat < 0) return;  // padding slot of the XCD-interleaved table
+// One output tile of one product (the whole work of a workgroup); lds holds
+// Lds<TILE, BF16, STAGE>::kBytes bytes.
+template <int TILE, bool BF16, int STAGE>
+__device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, const GemmTile tile,
+                                             unsigned char* __restrict__ lds) {
+    using TE = std::conditional_t<BF16, uint16_t, float>;
+    using G = Geo<TILE, BF16>;
+    using L = Lds<TILE, BF16, STAGE>;
+    constexpr int kEs = L::kEs;
+    constexpr int kBk = L::kBk;
+    constexpr int kMi = G::kMi, kNj = G::kNj;
+    constexpr int kL = G::kLoads;
+    constexpr bool kQLdsT = L::kQLdsT;
+    constexpr bool kTransQ = L::kTransQ;
+    constexpr int kS = L::kS;
+    constexpr int kBuf = L::kBuf;
+
     const MatInfo& mt = args.mats[tile.mat];
     const int rp = mt.rp, cp = mt.cp;
     const int ti = tile.ti, tj = tile.tj;
@@ -1004,6 +1018,33 @@ __global__ __launch_bounds__((Geo<TILE, BF16>::kThreads), (Geo<TILE, BF16>::kMin
     }
 }
 
+template <int TILE, bool BF16, int STAGE>
+__global__ __launch_bounds__((Geo<TILE, BF16>::kThreads), (Geo<TILE, BF16>::kMinWaves)) void ns_gemm_kernel(
+    NsArgs args) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds[Lds<TILE, BF16, STAGE>::kBytes];
+    const GemmTile tile = args.tiles[blockIdx.x];
+    if (tile.mat < 0) return;  // padding slot of the XCD-interleaved table
+    ns_gemm_tile<TILE, BF16, STAGE>(args, tile, lds);
+}
+
+// The 128-tile and 64-tile classes of one stage in one launch: table slots
+// [0, split) hold 128-tiles (bfloat16 or float32 products), the rest 64-tiles
+// (float32).  Both take 4 waves and fit two workgroups per CU, so the small
+// 64-tiles fill the CUs the 128-tiles leave idle instead of waiting for a
+// launch of their own.
+template <bool BF16, int STAGE>
+__global__ __launch_bounds__(256, 2) void ns_gemm_mixed_kernel(NsArgs args) {
+    static_assert(Geo<128, BF16>::kThreads == 256 && Geo<64, false>::kThreads == 256, "block size");
+    constexpr int kA = Lds<128, BF16, STAGE>::kBytes, kB = Lds<64, false, STAGE>::kBytes;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kA > kB ? kA : kB];
+    const GemmTile tile = args.tiles[blockIdx.x];
+    if (tile.mat < 0) return;  // padding slot of an XCD-interleaved table
+    if (int(blockIdx.x) < args.split)
+        ns_gemm_tile<128, BF16, STAGE>(args, tile, lds);
+    else
+        ns_gemm_tile<64, false, STAGE>(args, tile, lds);
+}
+
 template <int TILE, bool BF16>
 const char* stage_name(int stage) {
     static const char* const names[3] = {
@@ -1028,6 +1069,21 @@ hipError_t launch_stage(int stage, int n_tiles, const NsArgs& a, hipStream_t s) 
         case kStageA: ns_gemm_kernel<TILE, BF16, kStageA><<<grid, block, 0, s>>>(a); break;
         case kStageB: ns_gemm_kernel<TILE, BF16, kStageB><<<grid, block, 0, s>>>(a); break;
         default: ns_gemm_kernel<TILE, BF16, kStageX><<<grid, block, 0, s>>>(a); break;
+    }
+    return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch_mixed(int stage, int n_tiles, const NsArgs& a, hipStream_t s) {
+    static const char* const names[2][3] = {
+        {"ns_a_t128+64_f32", "ns_b_t128+64_f32", "ns_x_t128+64_f32"},
+        {"ns_a_t128+64_bf16", "ns_b_t128+64_bf16", "ns_x_t128+64_bf16"}};
+    LaunchTimer timer(names[BF16 ? 1 : 0][stage], s);
+    const dim3 grid{static_cast<unsigned>(n_tiles)}, block{256u};
+    switch (stage) {
+        case kStageA: ns_gemm_mixed_kernel<BF16, kStageA><<<grid, block, 0, s>>>(a); break;
+        case kStageB: ns_gemm_mixed_kernel<BF16, kStageB><<<grid, block, 0, s>>>(a); break;
+        default: ns_gemm_mixed_kernel<BF16, kStageX><<<grid, block, 0, s>>>(a); break;
     }
     return hipGetLastError();
 }
@@ -1072,14 +1128,34 @@ hipError_t launch_newton_schulz(const PlanView& p, void* ws, float* o, const Fus
             a.param_bf16 = fuse->param_dtype == MUON_DTYPE_BF16;
         }
         for (int stage = kStageA; stage <= kStageX; ++stage) {
+            auto count_of = [&](const TileClassDev& tc) {
+                return stage == kStageX ? tc.n_full : stage == kStageA ? tc.n_sym_a : tc.n_sym_b;
+            };
+            auto table_of = [&](const TileClassDev& tc) {
+                return stage == kStageX ? tc.full : stage == kStageA ? tc.sym_a : tc.sym_b;
+            };
+            // the 128- and 64-tile classes share one launch when both have tiles
+            // (the plan keeps a stage's class tables contiguous)
+            const TileClassDev& t128 = p.classes[1];
+            const TileClassDev& t64 = p.classes[2];
+            const bool mixed = count_of(t128) > 0 && count_of(t64) > 0 &&
+                               table_of(t128) + count_of(t128) == table_of(t64);
             for (int c = 0; c < p.n_classes; ++c) {
                 const TileClassDev& tc = p.classes[c];
-                const int count = stage == kStageX ? tc.n_full
-                                  : stage == kStageA ? tc.n_sym_a : tc.n_sym_b;
-                a.tiles = stage == kStageX ? tc.full : stage == kStageA ? tc.sym_a : tc.sym_b;
+                const int count = count_of(tc);
+                a.tiles = table_of(tc);
                 const bool cls_bf16 = bf16 && tc.tile != kF32NsTile;
-                const hipError_t e = cls_bf16 ? launch_class<true>(tc.tile, stage, count, a, s)
-                                              : launch_class<false>(tc.tile, stage, count, a, s);
+                hipError_t e;
+                if (mixed && c == 1) {
+                    a.split = count;
+                    e = bf16 ? launch_mixed<true>(stage, count + count_of(t64), a, s)
+                             : launch_mixed<false>(stage, count + count_of(t64), a, s);
+                } else if (mixed && c == 2) {
+                    continue;
+                } else {
+                    e = cls_bf16 ? launch_class<true>(tc.tile, stage, count, a, s)
+                                 : launch_class<false>(tc.tile, stage, count, a, s);
+                }
                 if (e != hipSuccess) return e;
             }
         }

@@ -35,13 +35,16 @@ int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 // GEMM tile size for a matrix whose NS orientation is r x c.  Large tiles
 // give the MFMA pipeline the operand reuse it needs; small matrices use small
-// tiles so that zero padding stays a small fraction of the work.  float32
-// products longer than kF32ChainK use at most 128-tiles: only those split
-// their accumulation chains (the 256-tile has no registers to spare), and
-// every contraction of a 256-tile is then at most c.
+// tiles so that zero padding stays a small fraction of the work.  Below a
+// shorter side of 1024 a 256-tile matrix has at most 3 x 3 upper-triangle
+// tiles and short contractions: such matrices fill 256 CUs poorly and their
+// launches are latency-bound, so they take 128-tiles.  float32 products
+// longer than kF32ChainK use at most 128-tiles: only those split their
+// accumulation chains (the 256-tile has no registers to spare), and every
+// contraction of a 256-tile is then at most c.
 constexpr int64_t kF32ChainK = 32768;
 int choose_tile(int64_t r, int64_t c, int gemm_mode) {
-    if (r >= 768 && (gemm_mode != MUON_GEMM_F32 || c <= kF32ChainK)) return 256;
+    if (r >= 1024 && (gemm_mode != MUON_GEMM_F32 || c <= kF32ChainK)) return 256;
     if (r >= 160) return 128;
     return 64;
 }
@@ -349,11 +352,18 @@ std::unique_ptr<WaveTables> build_wave(const muon_matrix_desc_t* d, int64_t n, i
     p->o_mats = reserve(p->mats.size() * sizeof(MatInfo));
     p->o_cp = reserve(p->chunk_prefix.size() * 4);
     p->o_kp = reserve(p->cast_prefix.size() * 4);
-    for (int c = 0; c < 3; ++c) {
-        p->o_sym_a[c] = reserve(p->sym_a[c].size() * sizeof(GemmTile));
-        p->o_sym_b[c] = reserve(p->sym_b[c].size() * sizeof(GemmTile));
-        p->o_full[c] = reserve(p->full[c].size() * sizeof(GemmTile));
-    }
+    // each stage's class tables back to back (a mixed launch of the 128- and
+    // 64-tile classes reads both as one table); every table holds a multiple of
+    // 8 slots, so the XCD of each slot (slot % 8) is kept
+    auto contiguous = [&](std::vector<GemmTile>* t, size_t* o) {
+        size_t bytes = 0;
+        for (int c = 0; c < 3; ++c) bytes += t[c].size() * sizeof(GemmTile);
+        o[0] = reserve(bytes);
+        for (int c = 1; c < 3; ++c) o[c] = o[c - 1] + t[c - 1].size() * sizeof(GemmTile);
+    };
+    contiguous(p->sym_a, p->o_sym_a);
+    contiguous(p->sym_b, p->o_sym_b);
+    contiguous(p->full, p->o_full);
     p->blob_bytes = std::max<size_t>(at, 256);
     return p;
 }

@@ -85,8 +85,10 @@ def test_apply_bit_exact(nsf, torch, dtype, shards):
 
 # ------------------------------------------------------- orthogonalization
 
+# every tile class (64: shorter side < 160; 128: < 1024; 256), ragged shapes in each
 SHAPES = [(1, 1), (1, 7), (7, 1), (3, 5), (64, 64), (65, 129), (129, 65), (130, 1000),
-          (1000, 130), (256, 512), (300, 300), (768, 769), (200, 1500), (1536, 800)]
+          (1000, 130), (256, 512), (300, 300), (768, 769), (200, 1500), (1536, 800),
+          (1100, 1301), (1301, 1100)]
 
 
 def _orth_case(nsf, torch, shapes, mode, ns_steps, seed=0):
@@ -205,11 +207,11 @@ def test_rank_deficient(nsf, torch, rank, mode):
 
 
 def test_orthogonalize_long_float32_contraction(nsf, torch):
-    """float32 products: a 768 x 33000 matrix (256-tile size, but a contraction
+    """float32 products: a 1024 x 33000 matrix (256-tile size, but a contraction
     past 32768) runs on 128-tiles whose Gram product restarts its accumulation
     chains after 1024 K blocks; O stays within the float32 tolerance."""
     say("orthogonalize long float32 contraction")
-    descs, uh, oh = _orth_case(nsf, torch, [(768, 33000), (33000, 768)], "f32", 5)
+    descs, uh, oh = _orth_case(nsf, torch, [(1024, 33000), (33000, 1024)], "f32", 5)
     for d in descs:
         want = mo.newton_schulz(mat(uh, d).astype(np.float64), 5)
         err = rel_fro(mat(oh, d), want)
