@@ -200,6 +200,59 @@ __global__ __launch_bounds__(256) void front_cast_kernel(const MatInfo* __restri
             }
         }
     };
+    // Rows whose length is not a multiple of 4 start at unaligned addresses:
+    // their G and M (or U) are read as aligned 4-element vectors covering the
+    // workgroup's elements (a vector is read whole when it lies inside the
+    // matrix, else element by element), M is stored for the workgroup's own
+    // elements only, and U goes through LDS to the iterate.  The values, and
+    // the order in which the sum of squares adds them, are those of the aligned
+    // path.  Vector at matrix-relative element a (a % 4 == 0; a < 0: none).
+    constexpr int kV = 5;  // vectors per thread: <= 1025 (wide) or 1088 (tall) per workgroup
+    auto loadv = [&](int64_t a, float gv[4], float mv[4]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) gv[q] = mv[q] = 0.f;
+        if (a < 0) return;
+        const int64_t e = mt.off + a;
+        if (a + 4 <= mt.numel) {
+            const float4 a4 = load4_stream((kStep ? g : u_in) + e);
+            gv[0] = a4.x, gv[1] = a4.y, gv[2] = a4.z, gv[3] = a4.w;
+            if (kStep) {
+                const float4 b4 = load4_stream(m + e);
+                mv[0] = b4.x, mv[1] = b4.y, mv[2] = b4.z, mv[3] = b4.w;
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (a + q < mt.numel) {
+                    gv[q] = (kStep ? g : u_in)[e + q];
+                    if (kStep) mv[q] = m[e + q];
+                }
+            }
+        }
+    };
+    // U of the vector's elements; with kStep, M is stored for those in [lo, hi)
+    auto updv = [&](int64_t a, int64_t lo, int64_t hi, const float gv[4], const float mv[4],
+                    float uv[4]) {
+        if (!kStep) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) uv[q] = gv[q];
+            return;
+        }
+        float m1[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            m1[q] = beta * mv[q] + gv[q];
+            uv[q] = nesterov ? beta * m1[q] + gv[q] : m1[q];
+        }
+        const int64_t e = mt.off + a;
+        if (a >= lo && a + 4 <= hi) {
+            store4_stream(m + e, make_float4(m1[0], m1[1], m1[2], m1[3]));
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (a + q >= lo && a + q < hi) m[e + q] = m1[q];
+        }
+    };
     float ss = 0.f;
     // X (NS orientation) at element offset at of this matrix, in its product type
     auto store_iter4 = [&](int64_t at, const float v[4]) {
@@ -239,6 +292,57 @@ __global__ __launch_bounds__(256) void front_cast_kernel(const MatInfo* __restri
             }
         }
     };
+    // tall_in for rows not a multiple of 4 long: the block's row segments are
+    // read as aligned vectors (row rr: the vectors from its first element's
+    // aligned start), U written into the block tile; then, in tall_in's order,
+    // the sum of squares, with the tile's entries outside R x C set to zero
+    auto tall_in_unaligned = [&](auto tr_tag) {
+        constexpr int TR = decltype(tr_tag)::value, TC = T * T / TR, kSegs = TC / 4;
+        constexpr int kVpr = TC / 4 + 1;  // vectors per row segment
+        const int nti = mt.rp / TC;
+        const int tj = t / nti, ti = t % nti;
+        const int ur0 = tj * TR, uc0 = ti * TC;
+        const int64_t C = mt.C;
+        const int64_t cw = uc0 < C ? (C - uc0 < TC ? C - uc0 : TC) : 0;  // real columns
+        float gv[kV][4], mv[kV][4];
+        int64_t av[kV];
+#pragma unroll
+        for (int k = 0; k < kV; ++k) {
+            const int v = k * 256 + int(threadIdx.x);
+            const int rr = v / kVpr, kk = v % kVpr, gr = ur0 + rr;
+            const int64_t lo = int64_t(gr) * C + uc0;
+            const int64_t a = (lo & ~int64_t(3)) + 4 * kk;
+            av[k] = (v < TR * kVpr && gr < mt.R && cw > 0 && a < lo + cw) ? a : -1;
+            loadv(av[k], gv[k], mv[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < kV; ++k) {
+            if (av[k] < 0) continue;
+            const int rr = (k * 256 + int(threadIdx.x)) / kVpr;
+            const int64_t lo = int64_t(ur0 + rr) * C + uc0;
+            float uv[4];
+            updv(av[k], lo, lo + cw, gv[k], mv[k], uv);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t el = av[k] + q;
+                if (el >= lo && el < lo + cw) tile[rr * (TC + 1) + int(el - lo)] = uv[q];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < kIters; ++it) {
+            const int seg = it * 256 + int(threadIdx.x);
+            const int rr = seg / kSegs, c4 = (seg % kSegs) * 4;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float* cell = &tile[rr * (TC + 1) + c4 + q];
+                const bool in = ur0 + rr < mt.R && c4 + q < cw;
+                const float u = in ? *cell : 0.f;
+                if (!in) *cell = 0.f;
+                ss = ss + u * u;
+            }
+        }
+    };
     // X[i][j], i = ti*TC + a, j = tj*TR + b = U[j][i] = block element (b, a); each
     // thread writes 4 consecutive elements of a row
     auto tall_out = [&](auto tr_tag) {
@@ -253,7 +357,47 @@ __global__ __launch_bounds__(256) void front_cast_kernel(const MatInfo* __restri
             store_iter4(int64_t(ti * TC + a) * mt.cp + tj * TR + b, v);
         }
     };
-    if (!tall) {
+    if (!tall && !vec) {
+        // wide, rows not a multiple of 4 long: the workgroup's elements of U are
+        // one flat run [lo, hi) of the matrix (its rows are contiguous)
+        const int64_t base = int64_t(t) * (T * T);
+        const int64_t last = base + T * T - 1;
+        const int i0 = int(base / mt.cp), j0 = int(base % mt.cp);
+        const int i1 = int(last / mt.cp), j1 = int(last % mt.cp) + 1;
+        const int64_t C = mt.C;
+        const int64_t lo = i0 < mt.R ? int64_t(i0) * C + (j0 < C ? j0 : C) : mt.numel;
+        const int64_t hi = i1 < mt.R ? int64_t(i1) * C + (j1 < C ? j1 : C) : mt.numel;
+        const int64_t a0 = lo & ~int64_t(3);
+        const int nv = int((hi - a0 + 3) >> 2);
+        float gv[kV][4], mv[kV][4];
+#pragma unroll
+        for (int k = 0; k < kV; ++k) {
+            const int v = k * 256 + int(threadIdx.x);
+            loadv(v < nv ? a0 + 4 * int64_t(v) : -1, gv[k], mv[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < kV; ++k) {
+            const int v = k * 256 + int(threadIdx.x);
+            if (v >= nv) continue;
+            float uv[4];
+            updv(a0 + 4 * int64_t(v), lo, hi, gv[k], mv[k], uv);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) tile[4 * v + q] = uv[q];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < kIters; ++it) {
+            const int e = j0 + (it * 256 + int(threadIdx.x)) * 4;
+            const int gr = i0 + e / mt.cp, gc = e % mt.cp;
+            float uv[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uv[q] = (gr < mt.R && gc + q < C) ? tile[int(int64_t(gr) * C + gc + q - a0)] : 0.f;
+                ss = ss + uv[q] * uv[q];
+            }
+            store_iter4(base + (it * 256 + int(threadIdx.x)) * 4, uv);
+        }
+    } else if (!tall) {
         // The iterate has U's own orientation: workgroup t takes the 4096
         // consecutive elements [4096 t, 4096 t + 4096) of the row-major rp x cp
         // iterate (rows padded to cp), thread tid the 4-element groups
@@ -276,6 +420,11 @@ __global__ __launch_bounds__(256) void front_cast_kernel(const MatInfo* __restri
             for (int q = 0; q < 4; ++q) ss = ss + uv[q] * uv[q];
             store_iter4(base + (it * 256 + int(threadIdx.x)) * 4, uv);
         }
+    } else if (!vec) {
+        if (tall_rows == 32)
+            tall_in_unaligned(std::integral_constant<int, 32>{});
+        else
+            tall_in_unaligned(std::integral_constant<int, 64>{});
     } else if (tall_rows == 32) {
         tall_in(std::integral_constant<int, 32>{});
     } else {
