@@ -70,21 +70,27 @@ def elementwise_bytes(wl, mode):
             "apply": 4 * n + 2 * wb * n}    # O read, W read + write
 
 
-KERNEL_SOURCES = ("k_ns_gemm.hip", "k_elementwise.hip", "k_norm_cast.hip")  # hashed with traffic
+def kernel_source(kernel):
+    """The source file that holds a kernel of the profile table."""
+    if kernel.startswith("ns_"):
+        return "k_ns_gemm.hip"
+    if kernel in ("front", "apply", "sumsq"):
+        return "k_elementwise.hip"
+    return "k_norm_cast.hip"  # front_cast, sumsq_cast, norm, cast
 
 
 def recorded_traffic(kernel, workload):
     """HBM bytes per launch (read + written) that profiler counters recorded for
-    this kernel on this workload, if the kernel sources are unchanged since;
-    otherwise None."""
+    this kernel on this workload, if the kernel's source file is unchanged
+    since; otherwise None."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"{workload}_traffic.json")
     try:
         rec = json.load(open(path))
-        for f in KERNEL_SOURCES:
-            src = os.path.join(ROOT, "newton_schulz_flat_amd", "csrc", f)
-            if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["sources_sha256"][f]:
-                return None
+        f = kernel_source(kernel)
+        src = os.path.join(ROOT, "newton_schulz_flat_amd", "csrc", f)
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["sources_sha256"][f]:
+            return None
         b = rec["per_launch_bytes"][kernel]
         return b["read"] + b["written"]
     except (OSError, KeyError, ValueError):
