@@ -76,8 +76,8 @@
  * front and raises rather than run on a bad mapping (FsdpMuon._validate_parameter_groups
  * on the page "core.distributed.fsdp.src.megatron_fsdp.experimental.muon";
  * the review answer on the page "feat(fsdp): expose HSDP and HFSDP through
- * the MFSDP v2 adapter" that an unsupported layout raises instead of being
- * silently mis-mapped).  Here every entry point returns MUON_OK (0) or a
+ * the MFSDP v2 adapter": an inconsistent layout is an error, never a quiet
+ * wrong mapping).  Here every entry point returns MUON_OK (0) or a
  * negative muon_status_t instead of raising: nothing is thrown across the
  * ABI.  Every check except MUON_ERR_HIP runs before anything is enqueued, so
  * a failed call leaves every buffer untouched.  muon_last_error() returns a
@@ -148,8 +148,8 @@ enum { MUON_GEMM_BF16_MFMA = 0, MUON_GEMM_F32 = 1 };
 
 /* Bytes of device workspace with which muon_step / muon_orthogonalize run
  * these descriptors in one wave, for this GEMM mode (the plan-building
- * analogue of the owner assignment "computed during initialization" in
- * FsdpMuon).  Host-only: makes no HIP call.  Validates the descriptors' shapes
+ * analogue of FsdpMuon's owner assignment, which is worked out once when the
+ * optimizer is set up).  Host-only: makes no HIP call.  Validates the descriptors' shapes
  * (not their bounds).  out_bytes: host pointer receiving the size. */
 int muon_workspace_bytes(const muon_matrix_desc_t* descs, int64_t n, int gemm_mode,
                          size_t* out_bytes);
@@ -157,8 +157,8 @@ int muon_workspace_bytes(const muon_matrix_desc_t* descs, int64_t n, int gemm_mo
 /* Smallest workspace with which the descriptors run at all: the largest
  * single matrix's intermediates.  Between this and muon_workspace_bytes() the
  * matrices run in waves whose intermediates fit the workspace given (the
- * FsdpMuon class docstring: the step processes one buffer's updates at a time
- * on the caller's stream).  Host-only, same validation as muon_workspace_bytes. */
+ * FsdpMuon class docstring: the step works through the buffers in turn on the
+ * caller's stream).  Host-only, same validation as muon_workspace_bytes. */
 int muon_workspace_min_bytes(const muon_matrix_desc_t* descs, int64_t n, int gemm_mode,
                              size_t* out_bytes);
 
@@ -199,9 +199,10 @@ int muon_orthogonalize(const float* u, float* o_out, int64_t n_elems,
  * "core.distributed.fsdp.src.megatron_fsdp.experimental.muon", FsdpMuon._step_group,
  * argument tensor_to_optimizer_group_index).  An array of groups lives in DEVICE
  * memory and is read by the kernels when they run, so a captured graph
- * replays with whatever values the array holds at replay time (the "optimizer
- * CUDA graph" support listed on the page "fix(fsdp): drop stale MFSDP v2 guard
- * rails ...", Megatron-Bridge PR #5933).  Values are not checked: NaN and
+ * replays with whatever values the array holds at replay time (optimizer
+ * CUDA-graph support is among the features the Megatron-Bridge #5933 commit
+ * message lists, quoted on the page "feat(fsdp): expose HSDP and HFSDP
+ * through the MFSDP v2 adapter", PR #6873).  Values are not checked: NaN and
  * infinities propagate; nesterov is true when non-zero. */
 typedef struct muon_group {
     float lr;
@@ -220,9 +221,10 @@ typedef struct muon_group {
  *                     aligned and laid out like params: every updated weight
  *                     is also stored there, rounded to nearest even (float32
  *                     master weights with a refreshed bfloat16 model copy: the
- *                     pages' optimizer "refreshes its model weights itself",
- *                     FsdpMuon class docstring and FsdpMuon.step; the
- *                     precision-aware optimizer of PR #5933's page).
+ *                     pages' optimizer updates the model weights from the
+ *                     optimizer's own copy, FsdpMuon class docstring and
+ *                     FsdpMuon.step; the precision-aware optimizer listed in the
+ *                     Megatron-Bridge #5933 commit message on the PR #6873 page).
  * Every other argument as muon_step.  Once the plan for a descriptor set
  * exists (built by the first call with that set, which synchronizes the
  * stream: make it outside graph capture), a call makes no allocation, memset
@@ -285,8 +287,8 @@ int muon_profile_end(muon_kernel_time_t* out, int max_entries, int* n_entries);
 /* Static name of a status code ("MUON_OK", "MUON_ERR_BAD_SHAPE", ...): the
  * kind of a rejected call, which the pages' optimizer reports by raising from
  * its up-front validation (FsdpMuon._validate_parameter_groups, page
- * "core.distributed.fsdp.src.megatron_fsdp.experimental.muon"; "raise rather
- * than mis-map", review answers on the page "feat(fsdp): expose HSDP and
+ * "core.distributed.fsdp.src.megatron_fsdp.experimental.muon"; errors rather
+ * than wrong mappings, review answers on the page "feat(fsdp): expose HSDP and
  * HFSDP through the MFSDP v2 adapter").  Any int is accepted; unknown codes
  * give "MUON_ERR_UNKNOWN".  The string is static: never free it. */
 const char* muon_status_string(int status);

@@ -2,7 +2,7 @@
 // prefixes and the grouped GEMM tile tables, cached per descriptor set.
 //
 // The plan is the single-device analogue of FsdpMuon's owner assignment,
-// which is "computed during initialization" and balances orthogonalization
+// which the optimizer works out once when it is set up and which balances orthogonalization
 // cost across buffers (page "core.distributed.fsdp.src.megatron_fsdp.
 // experimental.muon", class FsdpMuon; PR #6425 "Opt step" step 3 picks owners
 // by orthogonalization cost).  Here the same cost model orders matrices so

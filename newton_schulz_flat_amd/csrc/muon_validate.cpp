@@ -4,7 +4,7 @@
 // Loud validation follows FsdpMuon._validate_parameter_groups on the page
 // "core.distributed.fsdp.src.megatron_fsdp.experimental.muon" (parameters and
 // the buffers holding them are checked up front) and the error convention of
-// PR #6873 (a layout mismatch raises instead of silently mis-mapping shards).
+// PR #6873 (an inconsistent layout is an error, never a quiet wrong mapping of shards).
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
