@@ -436,8 +436,11 @@ struct StepPlan {
         if (dev != nullptr) {
             // Kernels of any stream may still read the tables.  Only reached
             // outside the cache's lock (plans are dropped after it is released).
-            (void)hipDeviceSynchronize();
-            (void)hipFree(dev);
+            // If the device cannot be synchronized (another stream is being
+            // captured in global mode), the tables are left allocated rather
+            // than freed while a launch may still read them.
+            if (hipDeviceSynchronize() == hipSuccess) (void)hipFree(dev);
+            else (void)hipGetLastError();
         }
     }
 };
