@@ -256,7 +256,10 @@ int muon_apply(void* params, int param_dtype, int64_t n_param_elems, const float
  * with MUON_ERR_WORKSPACE_TOO_SMALL before anything is enqueued.  The first
  * call with a new descriptor set on a device copies its launch tables into the
  * array and synchronizes `stream`; later calls with the same set copy nothing
- * and do not synchronize.  All calls on one GPU share its array, which keeps
+ * and do not synchronize.  Under graph capture only a call with the set whose
+ * tables are resident (the device's last one) can run: any other is rejected
+ * with MUON_ERR_BAD_ARG before anything is enqueued, leaving the resident
+ * tables in place.  All calls on one GPU share its array, which keeps
  * the last call's contents: calls that overlap on one GPU (different streams,
  * or threads without ordering) race and must not be made. */
 int muon_step_noalloc(void* params, int param_dtype, int64_t n_param_elems, const float* grads,

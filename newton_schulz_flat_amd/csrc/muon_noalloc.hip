@@ -97,7 +97,18 @@ extern "C" int muon_step_noalloc(void* params, int param_dtype, int64_t n_param_
     std::memcpy(&key[sizeof(int)], descs, size_t(n) * sizeof(muon_matrix_desc_t));
     if (ds.key != key) {
         // a new descriptor set: its tables go to the head of the scratch (once;
-        // later calls with the same set copy nothing and do not synchronize)
+        // later calls with the same set copy nothing and do not synchronize).
+        // The copy and the synchronization cannot be captured into a graph.
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        e = hipStreamIsCapturing(stream, &cs);
+        if (e != hipSuccess) return report_hip(st, e, "hipStreamIsCapturing");
+        if (cs == hipStreamCaptureStatusActive) {
+            st.code = MUON_ERR_BAD_ARG;
+            snprintf(st.msg, sizeof(st.msg),
+                     "the launch tables of this descriptor set are not resident: make one call "
+                     "with it outside graph capture first (it copies them and synchronizes)");
+            return report(st);
+        }
         std::shared_ptr<HostPlan> hp;
         if (build_host_plan(descs, n, gemm_mode, capacity, &hp, &st) != MUON_OK) return report(st);
         const size_t bytes = host_plan_blob_bytes(*hp);

@@ -88,3 +88,59 @@ def test_too_large_matrix_is_rejected(nsf, torch):
                               H["weight_decay"], H["beta"])
     torch.cuda.synchronize()
     assert torch.count_nonzero(mom).item() == 0
+
+
+def test_graph_capture_with_resident_tables(nsf, torch):
+    """A call whose descriptor set has its tables resident is captured into a
+    HIP graph; every replay equals an eager muon_step bit for bit.  A call with
+    another set under capture is rejected before anything is enqueued, and the
+    resident tables stay in place (the graph still replays correctly); outside
+    capture that other set then runs as usual."""
+    wl = wlm.small_mixed(54, count=4, max_side=300, param_dtype="bf16")
+    other = wlm.small_mixed(55, count=2, max_side=200, param_dtype="bf16")
+    args = (H["lr"], H["weight_decay"], H["beta"])
+    params, grads, mom = wlm.make_tensors(wl, "cuda", momentum_std=1e-3)
+    pe, me = params.clone(), mom.clone()
+    ws = torch.empty(nsf.muon_workspace_bytes(wl.descs, "bf16"), dtype=torch.uint8, device="cuda")
+    say("noalloc graph", wl.name)
+    # the set's tables become resident (eager call on throwaway copies)
+    nsf.muon_step_noalloc(params.clone(), grads, mom.clone(), wl.descs, *args)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph):
+            nsf.muon_step_noalloc(params, grads, mom, wl.descs, *args)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    def replay_and_compare(tag):
+        graph.replay()
+        nsf.muon_step(pe, grads, me, wl.descs, *args, workspace=ws)
+        torch.cuda.synchronize()
+        say("noalloc graph replay", tag)
+        assert np.array_equal(bits(host(params)), bits(host(pe))), tag
+        assert np.array_equal(bits(host(mom)), bits(host(me))), tag
+
+    replay_and_compare(0)
+    replay_and_compare(1)
+    # another set under capture: rejected, nothing enqueued, tables kept
+    p2, g2, m2 = wlm.make_tensors(other, "cuda", momentum_std=1e-3)
+    m2_before = host(m2)
+    probe = torch.zeros(4, device="cuda")
+    g_other = torch.cuda.CUDAGraph()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g_other):
+            with pytest.raises(nsf.MuonError, match="BAD_ARG"):
+                nsf.muon_step_noalloc(p2, g2, m2, other.descs, *args)
+            probe.add_(1.0)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(m2), m2_before)
+    replay_and_compare(2)
+    # outside capture the other set runs (its tables replace the resident ones)
+    say("noalloc other set eager", other.name)
+    want, got = _both(nsf, torch, other, "bf16")
+    assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
