@@ -141,6 +141,26 @@ def newton_schulz(update: np.ndarray, ns_steps: int) -> np.ndarray:
     return shape_scale(rows, cols) * out
 
 
+def newton_schulz_left_factor(gram: np.ndarray, ns_steps: int) -> np.ndarray:
+    """The same iteration for a wide or square U (rows <= cols), from its Gram
+    matrix ``U U^T`` alone (float64, rows x rows): the matrix ``F`` with
+    ``newton_schulz(U, ns_steps) == F @ U`` (the shape scale is 1 for such U).
+
+    Every step multiplies the iterate on the left by ``a I + b A + c A^2`` with
+    ``A = X X^T``; starting from ``X = U / (||U||_F + eps)`` each iterate is
+    therefore ``X = P U`` with ``A = P (U U^T) P^T`` and ``||U||_F^2`` the
+    trace of ``U U^T``.  For matrices too large to iterate on the host, the
+    columns of the orthogonalized update are ``F u_j``.
+    """
+    p = np.eye(gram.shape[0]) / (math.sqrt(np.trace(gram)) + NORM_EPS)
+    a, b, c = NS_COEFFS
+    for _ in range(ns_steps):
+        gram_x = p @ gram @ p.T
+        poly = b * gram_x + c * (gram_x @ gram_x)
+        p = a * p + poly @ p
+    return p
+
+
 # --------------------------------------------------------------------------
 # Step (6) of "Opt step": decoupled decay and update of the weights.
 # --------------------------------------------------------------------------

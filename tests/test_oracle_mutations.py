@@ -35,6 +35,18 @@ def _ns_variant(transposed_gram=False, spectral_norm=False, forget_transpose_bac
     return ns
 
 
+def _left_factor_variant(gram_once=False, no_norm=False):
+    def lf(gram, ns_steps):
+        scale = 1.0 if no_norm else 1.0 / (math.sqrt(np.trace(gram)) + mo.NORM_EPS)
+        p = np.eye(gram.shape[0]) * scale
+        a, b, c = mo.NS_COEFFS
+        for _ in range(ns_steps):
+            gx = p @ gram if gram_once else p @ gram @ p.T
+            p = a * p + (b * gx + c * (gx @ gx)) @ p
+        return p
+    return lf
+
+
 PIN_TESTS = [
     lambda: pins.test_momentum_constant_gradient_closed_form(True),
     lambda: pins.test_momentum_constant_gradient_closed_form(False),
@@ -51,6 +63,7 @@ PIN_TESTS = [
     lambda: pins.test_transposition((13, 4)),
     pins.test_sharded_scatter_equals_contiguous,
     pins.test_bf16_params_step_uses_exact_widening,
+    lambda: pins.test_left_factor_closed_form((6, 10), 5),
 ]
 
 
@@ -83,6 +96,8 @@ MUTATIONS = {
     "no_transpose_back": ("newton_schulz", _ns_variant(forget_transpose_back=True)),
     "eps_in_sqrt": ("newton_schulz", _ns_variant(eps_in_sqrt=True)),
     "scatter_ignores_stride": ("scatter_param", None),
+    "left_factor_gram_once": ("newton_schulz_left_factor", _left_factor_variant(gram_once=True)),
+    "left_factor_unnormalized": ("newton_schulz_left_factor", _left_factor_variant(no_norm=True)),
     "bf16_truncating_widen": ("bf16_bits_to_f64",
                               lambda b: (b.astype(np.uint32) << 15).view(np.float32)
                               .astype(np.float64)),

@@ -205,6 +205,37 @@ def test_newton_schulz_singular_value_closed_form(shape, steps):
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-12 * max(1.0, np.abs(want).max()))
 
 
+@pytest.mark.parametrize("shape", [(8, 8), (6, 10), (1, 5), (3, 40), (16, 48)])
+@pytest.mark.parametrize("steps", [0, 1, 5])
+def test_left_factor_closed_form(shape, steps):
+    """U = P diag(s) Q^T (rows <= cols)  =>  the Gram form's factor is
+    F = P diag(f^k(sigma) / s) P^T, sigma = s / (||s|| + eps), so that
+    F U = P diag(f^k(sigma)) Q^T: the singular-value closed form of the
+    iteration, reached from U U^T alone."""
+    rows, cols = shape
+    rng = np.random.default_rng([rows, cols, steps, 2])
+    p = orthonormal(rng, rows, rows)
+    q = orthonormal(rng, cols, rows)
+    s = rng.uniform(0.05, 2.0, rows)
+    u = (p * s) @ q.T
+    sigma = s / (np.sqrt(np.sum(s * s)) + EPS)
+    want = (p * (quintic_f64(sigma, steps) / s)) @ p.T
+    got = mo.newton_schulz_left_factor(u @ u.T, steps)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-11 * max(1.0, np.abs(want).max()))
+    np.testing.assert_allclose(got @ u, (p * quintic_f64(sigma, steps)) @ q.T, rtol=0,
+                               atol=1e-11)
+
+
+@pytest.mark.parametrize("rank", [1, 2, 4])
+def test_left_factor_matches_the_direct_iteration(rank):
+    """F U against newton_schulz(U) on random 4 x 30 inputs of full and lower rank."""
+    rng = np.random.default_rng([rank, 30])
+    u = rng.standard_normal((4, rank)) @ rng.standard_normal((rank, 30))
+    for steps in (1, 5):
+        got = mo.newton_schulz_left_factor(u @ u.T, steps) @ u
+        np.testing.assert_allclose(got, mo.newton_schulz(u, steps), rtol=0, atol=1e-12)
+
+
 def test_shape_scale_values():
     assert mo.shape_scale(14336, 4096) == math.sqrt(3.5)
     assert mo.shape_scale(4096, 14336) == 1.0
