@@ -79,3 +79,60 @@ def test_matrix_beyond_int32_elements(nsf, torch):
     assert err_norm <= TOL["bf16"]
     del u, o, u2, o2
     torch.cuda.empty_cache()
+
+
+def test_step_beyond_int32_elements_sharded(nsf, torch):
+    """The whole step (fused decay and update) on the same shape with float32
+    master weights cut into 8 slices 4096 elements apart: slices start past
+    2^31 in the params buffer.  M0 = 0, so M1 = G and U = G + beta G; the
+    normalization removes U's scale, so O = F G with F from G G^T.  Checks: M
+    equals G bit for bit everywhere, the gaps between slices are untouched,
+    and the weight change at sampled columns against the oracle's
+    decay-then-update with that O."""
+    n = ROWS * COLS
+    shards, gap = 8, 4096
+    per = n // shards
+    stride = per + gap
+    h = wlm.HYPER
+    descs = [(0, ROWS, COLS, 0, stride, shards)]
+    say("large step", ROWS, "x", COLS, "in", shards, "slices of", per)
+    params = torch.full((shards * stride,), 7.0, device="cuda")
+    for s in range(shards):
+        params[s * stride:s * stride + per] = wlm._randn(per, 0.02, wlm.seed_of("large", 1, s),
+                                                          "cuda")
+    grads = wlm._randn(n, 1e-3, wlm.seed_of("large", 2, 0), "cuda")
+    mom = torch.zeros_like(grads)
+    rng = np.random.default_rng(12)
+    cols = np.unique(np.concatenate([[0, COLS - 1], rng.choice(COLS, 2000, replace=False)]))
+    elem = (np.arange(ROWS)[:, None] * COLS + cols[None, :]).astype(np.int64)
+    dst = (elem // per) * stride + elem % per
+    dst_t = torch.from_numpy(dst.reshape(-1)).to("cuda")
+    w_before = params[dst_t].cpu().numpy().astype(np.float64).reshape(dst.shape)
+    ws = torch.empty(nsf.muon_workspace_bytes(descs, "bf16"), dtype=torch.uint8, device="cuda")
+    say("large step: muon_step, workspace", ws.numel(), "bytes")
+    nsf.muon_step(params, grads, mom, descs, h["lr"], h["weight_decay"], h["beta"],
+                  ns_steps=5, mode="bf16", workspace=ws)
+    torch.cuda.synchronize()
+    del ws
+    torch.cuda.empty_cache()
+    assert torch.equal(mom, grads)
+    for s in range(shards):
+        assert bool((params[s * stride + per:(s + 1) * stride] == 7.0).all()), s
+    w_after = params[dst_t].cpu().numpy().astype(np.float64).reshape(dst.shape)
+
+    say("large step: host Gram sum")
+    g2 = grads.view(ROWS, COLS)
+    gg = np.zeros((ROWS, ROWS))
+    for j0 in range(0, COLS, CHUNK):
+        gb = g2[:, j0:j0 + CHUNK].cpu().numpy().astype(np.float64)
+        gg += gb @ gb.T
+    f = mo.newton_schulz_left_factor(gg, 5)
+    idx = torch.from_numpy(cols).to("cuda")
+    o = f @ g2[:, idx].cpu().numpy().astype(np.float64)
+    lr, wd = mo.as_f32_value(h["lr"]), mo.as_f32_value(h["weight_decay"])
+    want = w_before - mo.apply_update(w_before, o, lr, wd)
+    err = rel_fro(w_before - w_after, want)
+    say("large step: weight change at sampled columns", err)
+    assert err <= TOL["bf16"] + 1e-4
+    del params, grads, mom, g2
+    torch.cuda.empty_cache()
