@@ -433,6 +433,44 @@ def test_zero_gradient_decays_exactly(nsf, torch):
         assert np.array_equal(param_slices(w1, d), want)
 
 
+@pytest.mark.parametrize("mode", ["f32", "bf16"])
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+def test_non_finite_gradient_stays_in_its_matrix(nsf, torch, mode, bad):
+    """A NaN or infinite gradient element (no special handling: it propagates
+    through the method's arithmetic) makes that matrix's whole update NaN, as
+    in the fp64 oracle, and changes nothing else: the other matrices' weights
+    and every other momentum element equal a clean run bit for bit."""
+    wl = wlm.small_mixed(12, count=5, max_side=260, param_dtype="bf16", shards=2)
+    params, grads, mom = _step_copies(wl, torch, momentum_std=1e-3)
+    p_clean, m_clean = params.clone(), mom.clone()
+    nsf.muon_step(p_clean, grads, m_clean, wl.descs, H["lr"], H["weight_decay"], H["beta"],
+                  mode=mode)
+    d_bad = wl.descs[2]
+    at = d_bad.offset + (d_bad.rows * d_bad.cols) // 2
+    g_bad = grads.clone()
+    g_bad[at] = bad
+    say("non-finite gradient", mode, bad, (d_bad.rows, d_bad.cols), at)
+    nsf.muon_step(params, g_bad, mom, wl.descs, H["lr"], H["weight_decay"], H["beta"], mode=mode)
+    gpu_sync(torch)
+    w1, wc = host(params), host(p_clean)
+    m1, mc = host(mom), host(m_clean)
+    with np.errstate(invalid="ignore"):
+        o_bad = mo.newton_schulz(np.where(np.arange(d_bad.rows * d_bad.cols) == (at - d_bad.offset),
+                                          bad, 1.0).reshape(d_bad.rows, d_bad.cols), 5)
+    assert np.isnan(o_bad).all()  # the oracle: the whole update is NaN
+    for d in wl.descs:
+        if d is d_bad:
+            assert np.isnan(mo.bf16_bits_to_f64(param_slices(w1, d))).all(), d
+        else:
+            assert np.array_equal(param_slices(w1, d), param_slices(wc, d)), d
+    diff = np.flatnonzero(bits(m1) != bits(mc))
+    assert list(diff) == [at]
+    if np.isnan(bad):
+        assert np.isnan(m1[at])
+    else:
+        assert m1[at] == bad
+
+
 # ------------------------------------------------------- batched workload
 
 @pytest.mark.parametrize("mode", ["f32", "bf16"])
