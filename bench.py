@@ -1,7 +1,7 @@
 """Benchmark of the MI355X Muon step (one GPU).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload owner] [--mode bf16]
-                    [--variant step|grouped|graph|master]
+                    [--variant step|grouped|graph|master|phases]
 
 One "step" is one whole ``muon_step`` call (momentum + Nesterov input,
 Frobenius normalization, 5 Newton-Schulz iterations, decay + apply) over the
@@ -17,7 +17,9 @@ Variants (same workload): ``grouped`` runs muon_step_grouped with two optimizer
 groups (attention and MLP matrices, different lr / weight decay / beta) read
 from a device table; ``graph`` captures that grouped step in a HIP graph and
 times graph replays; ``master`` keeps float32 master weights and refreshes a
-bfloat16 model copy in the same step.
+bfloat16 model copy in the same step; ``phases`` runs the step as its three
+separate entry points (muon_momentum, muon_orthogonalize, muon_apply), which
+times the standalone momentum and apply kernels.
 
 Prints one JSON line: matrices/s for the whole step, the Newton-Schulz
 algorithmic TFLOP/s and its fraction of the bf16 dense MFMA peak, the roofline
@@ -67,6 +69,7 @@ def elementwise_bytes(wl, mode):
     return {"front_cast": 12 * n + xb * n,  # G, M read; M written; first iterate written
             "front": 16 * n,                # G read, M read + write, U write (float32)
             "cast": 4 * n + xb * n,         # U read, X0 written
+            "sumsq_cast": 4 * n + xb * n,   # U read, first iterate written (muon_orthogonalize)
             "apply": 4 * n + 2 * wb * n}    # O read, W read + write
 
 
@@ -198,12 +201,19 @@ def measure(workload, mode, variant, steps, warmup):
     elif variant == "master":
         table = nsf.group_table([(h["lr"], h["weight_decay"], h["beta"], True)], "cuda:0")
         model_copy = params.to(torch.bfloat16)
+    elif variant == "phases":
+        u = torch.empty_like(grads)
+        o = torch.empty_like(grads)
     ws = torch.empty(nsf.muon_workspace_bytes(descs, mode), dtype=torch.uint8, device="cuda:0")
 
     def eager():
         if variant == "step":
             nsf.muon_step(params, grads, mom, descs, h["lr"], h["weight_decay"], h["beta"],
                           nesterov=h["nesterov"], ns_steps=h["ns_steps"], mode=mode, workspace=ws)
+        elif variant == "phases":
+            nsf.muon_momentum(grads, mom, u, descs, h["beta"], h["nesterov"])
+            nsf.muon_orthogonalize(u, o, descs, ns_steps=h["ns_steps"], mode=mode, workspace=ws)
+            nsf.muon_apply(params, o, descs, h["lr"], h["weight_decay"])
         else:
             nsf.muon_step_grouped(params, grads, mom, descs, table, ns_steps=h["ns_steps"],
                                   mode=mode, workspace=ws,
@@ -265,11 +275,13 @@ def measure(workload, mode, variant, steps, warmup):
             if variant == "step" else None
         per_kernel = {k: {"ms_per_step": v[0] / steps, "launches_per_step": v[1] / steps}
                       for k, v in sorted(kernels.items())}
-        for k in ("front_cast", "front", "cast", "apply"):
+        for k in ("front_cast", "front", "cast", "sumsq_cast", "apply"):
             if k in kernels:
                 per_kernel[k]["GB/s"] = ew[k] / (kernels[k][0] / kernels[k][1] * 1e-3) / 1e9
                 per_kernel[k]["frac_hbm"] = per_kernel[k]["GB/s"] / PEAK_HBM_GBS
     del params, grads, mom, ws
+    if variant == "phases":
+        del u, o
     torch.cuda.empty_cache()
     return {"wl": wl, "ms": ms, "value": wl.n * 1e3 / ms, "ns_tflops": ns_tflops,
             "ns_ms": ns_ms, "roofline": roof, "kernels": per_kernel}
@@ -290,7 +302,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="owner", choices=wlm.WORKLOADS)
     ap.add_argument("--mode", default="bf16", choices=["bf16", "f32"])
-    ap.add_argument("--variant", default="step", choices=["step", "grouped", "graph", "master"])
+    ap.add_argument("--variant", default="step",
+                    choices=["step", "grouped", "graph", "master", "phases"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-llama", action="store_true",
                     help="skip the extra llama-layer figures reported next to the owner share")

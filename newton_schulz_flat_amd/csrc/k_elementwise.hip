@@ -5,8 +5,8 @@
 // update slices to their shard destinations ("Opt step" steps 5-6,
 // FsdpMuon._apply_local_updates).
 //
-// All three are HBM-bound streams: each workgroup owns one chunk of
-// 256 x 4 x 8 consecutive elements of one matrix and moves them with 16-byte
+// All three are HBM-bound streams: each workgroup owns one chunk of 512
+// consecutive elements of one matrix (kEwChunk) and moves them with 16-byte
 // (float4) nontemporal loads and stores, consecutive lanes on consecutive
 // vectors.
 // Floating-point contraction is off so that every multiply and add rounds on
@@ -21,14 +21,19 @@ namespace muon {
 namespace {
 
 // Deterministic block sum of one float per thread (fixed shuffle tree, then
-// the 4 wave sums in order).
-__device__ __forceinline__ float block_sum(float v, float* lds4) {
+// the kWaves wave sums in order).
+template <int kWaves>
+__device__ __forceinline__ float block_sum(float v, float* lds) {
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    if (lane == 0) lds4[wave] = v;
+    if (lane == 0) lds[wave] = v;
     __syncthreads();
     float t = 0.f;
-    if (threadIdx.x == 0) t = ((lds4[0] + lds4[1]) + lds4[2]) + lds4[3];
+    if (threadIdx.x == 0) {
+        t = lds[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) t += lds[w];
+    }
     return t;
 }
 
@@ -37,11 +42,11 @@ __device__ __forceinline__ float block_sum(float v, float* lds4) {
 // U element e of a matrix at offset off lives at u[e] (grads layout) or, with
 // u_compact, at u[e - off + u_off] (the workspace's compact U region).
 template <int kMode>
-__global__ __launch_bounds__(kEwThreads) void front_kernel(
+__global__ __launch_bounds__(kFrontThreads) void front_kernel(
     const MatInfo* __restrict__ mats, const int32_t* __restrict__ prefix, int n,
     const float* __restrict__ g, float* __restrict__ m, float* __restrict__ u_base,
     int u_compact, float* __restrict__ partial, Hyper h) {
-    __shared__ float lds4[4];
+    __shared__ float lds_w[kFrontThreads / 64];
     const int blk = blockIdx.x;
     const int mi = owner_of(prefix, n, blk);
     const HyperVals hv = hyper_for(h, mats[mi]);
@@ -54,8 +59,8 @@ __global__ __launch_bounds__(kEwThreads) void front_kernel(
     const int64_t ud = u_compact ? mats[mi].u_off - off : int64_t(0);
     float ss = 0.f;
 #pragma unroll
-    for (int it = 0; it < kEwIters; ++it) {
-        const int64_t e = base + (int64_t(it) * kEwThreads + threadIdx.x) * kEwVec;
+    for (int it = 0; it < kFrontIters; ++it) {
+        const int64_t e = base + (int64_t(it) * kFrontThreads + threadIdx.x) * kEwVec;
         if (e + kEwVec <= end) {
             float4 uv;
             if (kMode == 0) {
@@ -100,7 +105,7 @@ __global__ __launch_bounds__(kEwThreads) void front_kernel(
         }
     }
     if (partial != nullptr) {
-        const float t = block_sum(ss, lds4);
+        const float t = block_sum<kFrontThreads / 64>(ss, lds_w);
         if (threadIdx.x == 0) partial[blk] = t;
     }
 }
@@ -127,7 +132,7 @@ __device__ __forceinline__ void store_w1(uint16_t* p, float v) { *p = bf16_rne(v
 // O of the matrix at o[off ...] (grads layout) or, with o_compact, at
 // o[u_off ...] (the workspace's compact region).
 template <typename TW>
-__global__ __launch_bounds__(kEwThreads) void apply_kernel(
+__global__ __launch_bounds__(kApplyThreads) void apply_kernel(
     const MatInfo* __restrict__ mats, const int32_t* __restrict__ prefix, int n,
     TW* __restrict__ w, const float* __restrict__ o, int o_compact, Hyper h,
     uint16_t* __restrict__ copy) {
@@ -141,8 +146,8 @@ __global__ __launch_bounds__(kEwThreads) void apply_kernel(
     const bool sharded = slice != numel;
     const int64_t base = int64_t(blk - mt.chunk_begin) * kEwChunk;
 #pragma unroll
-    for (int it = 0; it < kEwIters; ++it) {
-        const int64_t j = base + (int64_t(it) * kEwThreads + threadIdx.x) * kEwVec;
+    for (int it = 0; it < kApplyIters; ++it) {
+        const int64_t j = base + (int64_t(it) * kApplyThreads + threadIdx.x) * kEwVec;
         if (j + kEwVec <= numel) {
             // slices are multiples of 8 long when sharded: a vector never straddles two
             int64_t dst = poff + j;
@@ -179,7 +184,7 @@ hipError_t launch_front(const PlanView& p, const float* grads, float* momentum, 
                         bool compact, float* partial, const Hyper& h, hipStream_t s) {
     if (p.total_chunks == 0) return hipSuccess;
     LaunchTimer timer("front", s);
-    front_kernel<0><<<dim3(unsigned(p.total_chunks)), dim3(kEwThreads), 0, s>>>(
+    front_kernel<0><<<dim3(unsigned(p.total_chunks)), dim3(kFrontThreads), 0, s>>>(
         p.mats, p.chunk_prefix, p.n, grads, momentum, u, compact ? 1 : 0, partial, h);
     return hipGetLastError();
 }
@@ -187,7 +192,7 @@ hipError_t launch_front(const PlanView& p, const float* grads, float* momentum, 
 hipError_t launch_sumsq(const PlanView& p, const float* u, float* partial, hipStream_t s) {
     if (p.total_chunks == 0) return hipSuccess;
     LaunchTimer timer("sumsq", s);
-    front_kernel<1><<<dim3(unsigned(p.total_chunks)), dim3(kEwThreads), 0, s>>>(
+    front_kernel<1><<<dim3(unsigned(p.total_chunks)), dim3(kFrontThreads), 0, s>>>(
         p.mats, p.chunk_prefix, p.n, nullptr, nullptr, const_cast<float*>(u), 0, partial, Hyper{});
     return hipGetLastError();
 }
@@ -196,7 +201,7 @@ hipError_t launch_apply(const PlanView& p, void* params, int param_dtype, const 
                         bool compact, const Hyper& h, uint16_t* model_copy, hipStream_t s) {
     if (p.total_chunks == 0) return hipSuccess;
     LaunchTimer timer("apply", s);
-    const dim3 grid{static_cast<unsigned>(p.total_chunks)}, block{kEwThreads};
+    const dim3 grid{static_cast<unsigned>(p.total_chunks)}, block{kApplyThreads};
     const int oc = compact ? 1 : 0;
     if (param_dtype == MUON_DTYPE_BF16)
         apply_kernel<uint16_t><<<grid, block, 0, s>>>(p.mats, p.chunk_prefix, p.n,

@@ -15,13 +15,16 @@ namespace muon {
 
 // ---------------------------------------------------------------- geometry
 
-// Elements handled by one workgroup of the elementwise kernels
-// (256 threads x 4 elements x 8 iterations).  One float partial sum of
-// squares is produced per chunk.
-constexpr int kEwThreads = 256;
+// Elements handled by one workgroup of the elementwise kernels: 512, as
+// 128 threads x one float4 for the momentum kernel (two 16-byte loads per
+// thread) and 64 threads x two float4 for the apply kernel (whose bfloat16
+// weight loads are 8 bytes).  Small chunks keep many workgroups in flight
+// per CU; one float partial sum of squares is produced per chunk.
 constexpr int kEwVec = 4;
-constexpr int kEwIters = 8;
-constexpr int64_t kEwChunk = int64_t(kEwThreads) * kEwVec * kEwIters;
+constexpr int kFrontThreads = 128, kFrontIters = 1;
+constexpr int kApplyThreads = 64, kApplyIters = 2;
+constexpr int64_t kEwChunk = int64_t(kFrontThreads) * kEwVec * kFrontIters;
+static_assert(kEwChunk == int64_t(kApplyThreads) * kEwVec * kApplyIters, "one chunk size");
 
 // Square tile of the normalize/cast/orient kernel.
 constexpr int kCastTile = 64;
