@@ -103,7 +103,9 @@ extern "C" {
  *
  *   offset        element offset of the row-major rows x cols matrix in the
  *                 flat grads / momentum (and update) buffers; multiple of 4.
- *   rows, cols    matrix shape, each >= 1.
+ *   rows, cols    matrix shape, each >= 1 and <= 2^20, rows*cols <= 2^34;
+ *                 a set's matrices hold at most 2^36 elements in total
+ *                 (MUON_ERR_BAD_SHAPE otherwise).
  *   param_offset  element offset of slice 0 in the flat params buffer.
  *   shard_stride  distance in elements between consecutive slices in params
  *                 (>= rows*cols/n_shards; ignored when n_shards == 1).

@@ -41,13 +41,14 @@ __device__ __forceinline__ float block_sum(float v, float* lds) {
 // kMode 1: partial sums of U^2 only (U given).
 // U element e of a matrix at offset off lives at u[e] (grads layout) or, with
 // u_compact, at u[e - off + u_off] (the workspace's compact U region).
+// Workgroup x of a launch handles chunk chunk0 + x.
 template <int kMode>
 __global__ __launch_bounds__(kFrontThreads) void front_kernel(
     const MatInfo* __restrict__ mats, const int32_t* __restrict__ prefix, int n,
-    const float* __restrict__ g, float* __restrict__ m, float* __restrict__ u_base,
-    int u_compact, float* __restrict__ partial, Hyper h) {
+    int32_t chunk0, const float* __restrict__ g, float* __restrict__ m,
+    float* __restrict__ u_base, int u_compact, float* __restrict__ partial, Hyper h) {
     __shared__ float lds_w[kFrontThreads / 64];
-    const int blk = blockIdx.x;
+    const int blk = chunk0 + int(blockIdx.x);
     const int mi = owner_of(prefix, n, blk);
     const HyperVals hv = hyper_for(h, mats[mi]);
     const float beta = hv.beta;
@@ -134,9 +135,9 @@ __device__ __forceinline__ void store_w1(uint16_t* p, float v) { *p = bf16_rne(v
 template <typename TW>
 __global__ __launch_bounds__(kApplyThreads) void apply_kernel(
     const MatInfo* __restrict__ mats, const int32_t* __restrict__ prefix, int n,
-    TW* __restrict__ w, const float* __restrict__ o, int o_compact, Hyper h,
+    int32_t chunk0, TW* __restrict__ w, const float* __restrict__ o, int o_compact, Hyper h,
     uint16_t* __restrict__ copy) {
-    const int blk = blockIdx.x;
+    const int blk = chunk0 + int(blockIdx.x);
     const int mi = owner_of(prefix, n, blk);
     const MatInfo& mt = mats[mi];
     const HyperVals hv = hyper_for(h, mt);
@@ -178,40 +179,60 @@ __global__ __launch_bounds__(kApplyThreads) void apply_kernel(
     }
 }
 
+// A launch's grid counts at most 2^32 - 1 work-items: sets of more than
+// kEwGridChunks chunks (8 G elements) run as several launches in chunk order.
+constexpr int64_t kEwGridChunks = int64_t(1) << 24;
+static_assert(kEwGridChunks * kFrontThreads < (int64_t(1) << 32), "front grid");
+static_assert(kEwGridChunks * kApplyThreads < (int64_t(1) << 32), "apply grid");
+
+template <typename F>
+hipError_t for_each_grid(int64_t total, F launch) {
+    for (int64_t c0 = 0; c0 < total; c0 += kEwGridChunks) {
+        launch(int32_t(c0), dim3(unsigned(std::min(kEwGridChunks, total - c0))));
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 }  // namespace
 
 hipError_t launch_front(const PlanView& p, const float* grads, float* momentum, float* u,
                         bool compact, float* partial, const Hyper& h, hipStream_t s) {
     if (p.total_chunks == 0) return hipSuccess;
     LaunchTimer timer("front", s);
-    front_kernel<0><<<dim3(unsigned(p.total_chunks)), dim3(kFrontThreads), 0, s>>>(
-        p.mats, p.chunk_prefix, p.n, grads, momentum, u, compact ? 1 : 0, partial, h);
-    return hipGetLastError();
+    return for_each_grid(p.total_chunks, [&](int32_t c0, dim3 grid) {
+        front_kernel<0><<<grid, dim3(kFrontThreads), 0, s>>>(
+            p.mats, p.chunk_prefix, p.n, c0, grads, momentum, u, compact ? 1 : 0, partial, h);
+    });
 }
 
 hipError_t launch_sumsq(const PlanView& p, const float* u, float* partial, hipStream_t s) {
     if (p.total_chunks == 0) return hipSuccess;
     LaunchTimer timer("sumsq", s);
-    front_kernel<1><<<dim3(unsigned(p.total_chunks)), dim3(kFrontThreads), 0, s>>>(
-        p.mats, p.chunk_prefix, p.n, nullptr, nullptr, const_cast<float*>(u), 0, partial, Hyper{});
-    return hipGetLastError();
+    return for_each_grid(p.total_chunks, [&](int32_t c0, dim3 grid) {
+        front_kernel<1><<<grid, dim3(kFrontThreads), 0, s>>>(
+            p.mats, p.chunk_prefix, p.n, c0, nullptr, nullptr, const_cast<float*>(u), 0,
+            partial, Hyper{});
+    });
 }
 
 hipError_t launch_apply(const PlanView& p, void* params, int param_dtype, const float* o,
                         bool compact, const Hyper& h, uint16_t* model_copy, hipStream_t s) {
     if (p.total_chunks == 0) return hipSuccess;
     LaunchTimer timer("apply", s);
-    const dim3 grid{static_cast<unsigned>(p.total_chunks)}, block{kApplyThreads};
+    const dim3 block{kApplyThreads};
     const int oc = compact ? 1 : 0;
-    if (param_dtype == MUON_DTYPE_BF16)
-        apply_kernel<uint16_t><<<grid, block, 0, s>>>(p.mats, p.chunk_prefix, p.n,
-                                                      static_cast<uint16_t*>(params), o, oc, h,
-                                                      nullptr);
-    else
-        apply_kernel<float><<<grid, block, 0, s>>>(p.mats, p.chunk_prefix, p.n,
-                                                   static_cast<float*>(params), o, oc, h,
-                                                   model_copy);
-    return hipGetLastError();
+    return for_each_grid(p.total_chunks, [&](int32_t c0, dim3 grid) {
+        if (param_dtype == MUON_DTYPE_BF16)
+            apply_kernel<uint16_t><<<grid, block, 0, s>>>(p.mats, p.chunk_prefix, p.n, c0,
+                                                          static_cast<uint16_t*>(params), o, oc,
+                                                          h, nullptr);
+        else
+            apply_kernel<float><<<grid, block, 0, s>>>(p.mats, p.chunk_prefix, p.n, c0,
+                                                       static_cast<float*>(params), o, oc, h,
+                                                       model_copy);
+    });
 }
 
 }  // namespace muon

@@ -38,9 +38,12 @@ constexpr int kF32NsTile = 64;
 // Alignment of every workspace region, in bytes.
 constexpr size_t kWsAlign = 256;
 
-// Largest accepted matrix side and element count.
+// Largest accepted matrix side and element count, and element count of a
+// whole descriptor set (2^36 float32 elements are 256 GiB per buffer; the
+// bound keeps every chunk and tile count of a set within int32).
 constexpr int64_t kMaxSide = int64_t(1) << 20;
 constexpr int64_t kMaxNumel = int64_t(1) << 34;
+constexpr int64_t kMaxSetNumel = int64_t(1) << 36;
 constexpr int kMaxNsSteps = 64;
 constexpr int kMaxGroups = 65536;  // optimizer groups per muon_step_grouped call
 

@@ -29,6 +29,7 @@ int check_desc_shapes(const muon_matrix_desc_t* d, int64_t n, Status* st, int64_
     if (n > 0 && d == nullptr) return fail(st, MUON_ERR_NULL_POINTER, "descs is NULL");
     if (n > (int64_t(1) << 24))
         return fail(st, MUON_ERR_BAD_ARG, "descriptor count n = %lld is too large", (long long)n);
+    int64_t set_numel = 0;
     for (int64_t i = 0; i < n; ++i) {
         const muon_matrix_desc_t& m = d[i];
         if (m.rows < 1 || m.cols < 1)
@@ -37,6 +38,11 @@ int check_desc_shapes(const muon_matrix_desc_t* d, int64_t n, Status* st, int64_
         if (m.rows > kMaxSide || m.cols > kMaxSide || m.rows * m.cols > kMaxNumel)
             return fail(st, MUON_ERR_BAD_SHAPE, "descs[%lld]: shape %lld x %lld is too large",
                         (long long)i, (long long)m.rows, (long long)m.cols);
+        set_numel += m.rows * m.cols;
+        if (set_numel > kMaxSetNumel)
+            return fail(st, MUON_ERR_BAD_SHAPE,
+                        "descs[0..%lld] hold more than %lld elements in total", (long long)i,
+                        (long long)kMaxSetNumel);
         if (m.group < 0 || m.group >= n_groups)
             return fail(st, MUON_ERR_BAD_ARG, "descs[%lld]: group %d outside [0, %lld)",
                         (long long)i, m.group, (long long)n_groups);

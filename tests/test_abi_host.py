@@ -115,6 +115,16 @@ def test_workspace_bytes_rejects_bad_shapes(lib, item, code):
     assert lib.muon_last_error() != b""
 
 
+def test_workspace_bytes_bounds_the_whole_set(lib):
+    big = 1 << 17  # 2^17 x 2^17 = 2^34 elements, the largest matrix
+    four = [(k << 34, big, big) for k in range(4)]           # 2^36 in total
+    rc, b = ws_bytes(lib, four)
+    assert rc == 0 and b > 0
+    rc, _ = ws_bytes(lib, four + [(4 << 34, 1, 4)])          # four elements more
+    assert rc == ERR["BAD_SHAPE"]
+    assert b"in total" in lib.muon_last_error()
+
+
 def test_workspace_bytes_accepts_largest_side(lib):
     for shape in [(0, 1 << 20, 1), (0, 1, 1 << 20)]:
         rc, b = ws_bytes(lib, [shape])

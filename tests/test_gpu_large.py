@@ -1,4 +1,8 @@
-"""One matrix of more than 2^31 elements through muon_orthogonalize (C ABI).
+"""Sizes beyond int32 element counts and beyond one launch grid (C ABI).
+
+One matrix of more than 2^31 elements through muon_orthogonalize and
+muon_step; and a set of more than 2^24 elementwise chunks through
+muon_momentum and muon_apply, whose kernels then run as several launches.
 
 2100 x 2^20 (the longest side the library takes): every kernel indexes it
 with 64-bit offsets; bfloat16 products on 256-tiles, rows padded to 2304,
@@ -17,6 +21,7 @@ import pytest
 
 import workloads as wlm
 from oracle import muon_oracle as mo
+from oracle import same_order as so
 from tests.gpu_helpers import TOL, rel_fro, say
 
 pytestmark = pytest.mark.gpu
@@ -135,4 +140,52 @@ def test_step_beyond_int32_elements_sharded(nsf, torch):
     say("large step: weight change at sampled columns", err)
     assert err <= TOL["bf16"] + 1e-4
     del params, grads, mom, g2
+    torch.cuda.empty_cache()
+
+
+def test_elementwise_over_two_launch_grids(nsf, torch):
+    """A set of 8.59 G elements (8 matrices of 1024 x 2^20 and one of
+    1024 x 1024) is more than 2^24 workgroups of 512 elements, so the momentum
+    and apply kernels each run as two launches.  Sampled elements (the last of
+    the first grid, the first of the second, the ends of the set, and random
+    ones on both sides) bit-exact against the same-order float32 reference."""
+    shapes = [(1024, 2 ** 20)] * 8 + [(1024, 1024)]
+    descs, n = [], 0
+    for r, c in shapes:
+        descs.append((n, r, c))
+        n += r * c
+    first_grid = 2 ** 24 * 512  # elements the first launch covers
+    assert n > first_grid
+    h = wlm.HYPER
+    say("two grids:", n, "elements")
+    rng = np.random.default_rng(13)
+    idx = np.unique(np.concatenate([
+        [0, 1, first_grid - 5, first_grid - 1, first_grid, first_grid + 1, n - 2, n - 1],
+        rng.integers(0, n, 20000), rng.integers(first_grid, n, 4000)])).astype(np.int64)
+    idx_t = torch.from_numpy(idx).to("cuda")
+    grads = wlm._randn(n, 1e-3, wlm.seed_of("grids", 0, 0), "cuda")
+    mom = wlm._randn(n, 1e-3, wlm.seed_of("grids", 1, 0), "cuda")
+    g_s = grads[idx_t].cpu().numpy()
+    m_s = mom[idx_t].cpu().numpy()
+    u = torch.empty_like(grads)
+    say("two grids: muon_momentum")
+    nsf.muon_momentum(grads, mom, u, descs, h["beta"], h["nesterov"])
+    torch.cuda.synchronize()
+    m1, u1 = so.front(g_s, m_s, h["beta"], h["nesterov"])
+    assert np.array_equal(mom[idx_t].cpu().numpy().view(np.uint32), m1.view(np.uint32))
+    assert np.array_equal(u[idx_t].cpu().numpy().view(np.uint32), u1.view(np.uint32))
+    del grads, mom
+    torch.cuda.empty_cache()
+
+    params = wlm._randn(n, 0.02, wlm.seed_of("grids", 2, 0), "cuda").to(torch.bfloat16)
+    torch.cuda.empty_cache()
+    w_s = params[idx_t].view(torch.int16).cpu().numpy().view(np.uint16)
+    o_s = u[idx_t].cpu().numpy()
+    say("two grids: muon_apply")
+    nsf.muon_apply(params, u, descs, h["lr"], h["weight_decay"])
+    torch.cuda.synchronize()
+    want = so.apply(w_s, o_s, h["lr"], h["weight_decay"], "bf16")
+    got = params[idx_t].view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+    del params, u
     torch.cuda.empty_cache()
