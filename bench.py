@@ -22,7 +22,8 @@ separate entry points (muon_momentum, muon_orthogonalize, muon_apply), which
 times the standalone momentum and apply kernels.
 
 Prints one JSON line: matrices/s for the whole step, the Newton-Schulz
-algorithmic TFLOP/s and its fraction of the bf16 dense MFMA peak, the roofline
+algorithmic TFLOP/s and its fraction of the bf16 dense MFMA peak (with the
+dense-equivalent rate, counting full products, beside it), the roofline
 of the dominant kernel (per-launch durations from HIP events recorded on the
 launch stream during the timed region), and the CPU oracle timed on a bounded
 sample of the same workload (for the owner share: of one layer, times 32).
@@ -59,6 +60,13 @@ def stage_flops(wl, ns_steps):
         for k, v in ns_flops(r, c).items():
             tot[k] += v
     return tot  # per iteration (one launch per stage and tile size)
+
+
+def dense_flops(wl):
+    """Flops of one iteration counted as dense products (full A, A^2 and B X):
+    4 r^2 c + 2 r^3 per matrix, reported beside the algorithmic count."""
+    return sum(4 * r * r * c + 2 * r ** 3
+               for r, c in ((min(d.rows, d.cols), max(d.rows, d.cols)) for d in wl.descs))
 
 
 def elementwise_bytes(wl, mode):
@@ -248,10 +256,11 @@ def measure(workload, mode, variant, steps, warmup):
     fl = stage_flops(wl, h["ns_steps"])
     ns_alg = sum(fl.values()) * h["ns_steps"]
     ew = elementwise_bytes(wl, mode)
-    ns_ms, ns_tflops, roof, per_kernel = None, None, None, {}
+    ns_ms, ns_tflops, ns_dense, roof, per_kernel = None, None, None, None, {}
     if kernels:  # eager launches (graph replays carry no per-kernel events)
         ns_ms = sum(v[0] for k, v in kernels.items() if k.startswith("ns_")) / steps
         ns_tflops = ns_alg / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else 0.0
+        ns_dense = dense_flops(wl) * h["ns_steps"] / (ns_ms * 1e-3) / 1e12 if ns_ms > 0 else 0.0
         # dominant kernel = largest total time; its algorithmic work per launch
         name, (tot_ms, launches) = max(kernels.items(), key=lambda kv: kv[1][0])
         avg_s = tot_ms / launches * 1e-3
@@ -284,7 +293,8 @@ def measure(workload, mode, variant, steps, warmup):
         del u, o
     torch.cuda.empty_cache()
     return {"wl": wl, "ms": ms, "value": wl.n * 1e3 / ms, "ns_tflops": ns_tflops,
-            "ns_ms": ns_ms, "roofline": roof, "kernels": per_kernel}
+            "ns_dense_equivalent_tflops": ns_dense, "ns_ms": ns_ms, "roofline": roof,
+            "kernels": per_kernel}
 
 
 #: profiles/<name>_traffic.json of each workload
@@ -361,6 +371,7 @@ def main():
         "ns_frac_of_peak": None if r["ns_tflops"] is None
         else r["ns_tflops"] / PEAK_TFLOPS[args.mode],
         "ns_ms_per_step": r["ns_ms"],
+        "ns_dense_equivalent_tflops": r["ns_dense_equivalent_tflops"],
         "roofline": r["roofline"],
         "kernels": r["kernels"],
     }

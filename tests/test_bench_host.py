@@ -38,6 +38,13 @@ def test_stage_flops_take_the_shorter_side():
     assert bench.stage_flops(wl, 5) == want
 
 
+def test_dense_flops_count_full_products():
+    wl = wlm._contiguous("t", [(3, 7), (7, 3), (5, 5)], ["w", "t", "s"], "bf16", 0.02, 1e-3)
+    # full A = X X^T (2 r^2 c), full A A (2 r^3), full B X (2 r^2 c)
+    want = sum(2 * r * r * c + 2 * r ** 3 + 2 * r * r * c for r, c in [(3, 7), (3, 7), (5, 5)])
+    assert bench.dense_flops(wl) == want
+
+
 def test_elementwise_bytes_per_element():
     wl = wlm._contiguous("t", [(8, 16)], ["w"], "bf16", 0.02, 1e-3)
     n = 8 * 16
