@@ -1,7 +1,7 @@
 """Benchmark of the MI355X Muon step (one GPU).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload owner] [--mode bf16]
-                    [--variant step|grouped|graph|master|phases]
+                    [--variant step|grouped|graph|master|phases|noalloc]
 
 One "step" is one whole ``muon_step`` call (momentum + Nesterov input,
 Frobenius normalization, 5 Newton-Schulz iterations, decay + apply) over the
@@ -19,7 +19,9 @@ from a device table; ``graph`` captures that grouped step in a HIP graph and
 times graph replays; ``master`` keeps float32 master weights and refreshes a
 bfloat16 model copy in the same step; ``phases`` runs the step as its three
 separate entry points (muon_momentum, muon_orthogonalize, muon_apply), which
-times the standalone momentum and apply kernels.
+times the standalone momentum and apply kernels; ``noalloc`` runs
+muon_step_noalloc (intermediates in the library's fixed per-GPU scratch array,
+matrices in waves that fit it).
 
 Prints one JSON line: matrices/s for the whole step, the Newton-Schulz
 algorithmic TFLOP/s and its fraction of the bf16 dense MFMA peak (with the
@@ -212,12 +214,17 @@ def measure(workload, mode, variant, steps, warmup):
     elif variant == "phases":
         u = torch.empty_like(grads)
         o = torch.empty_like(grads)
-    ws = torch.empty(nsf.muon_workspace_bytes(descs, mode), dtype=torch.uint8, device="cuda:0")
+    ws = torch.empty(0 if variant == "noalloc" else nsf.muon_workspace_bytes(descs, mode),
+                     dtype=torch.uint8, device="cuda:0")
 
     def eager():
         if variant == "step":
             nsf.muon_step(params, grads, mom, descs, h["lr"], h["weight_decay"], h["beta"],
                           nesterov=h["nesterov"], ns_steps=h["ns_steps"], mode=mode, workspace=ws)
+        elif variant == "noalloc":
+            nsf.muon_step_noalloc(params, grads, mom, descs, h["lr"], h["weight_decay"],
+                                  h["beta"], nesterov=h["nesterov"], ns_steps=h["ns_steps"],
+                                  mode=mode)
         elif variant == "phases":
             nsf.muon_momentum(grads, mom, u, descs, h["beta"], h["nesterov"])
             nsf.muon_orthogonalize(u, o, descs, ns_steps=h["ns_steps"], mode=mode, workspace=ws)
@@ -313,7 +320,7 @@ def main():
     ap.add_argument("--workload", default="owner", choices=wlm.WORKLOADS)
     ap.add_argument("--mode", default="bf16", choices=["bf16", "f32"])
     ap.add_argument("--variant", default="step",
-                    choices=["step", "grouped", "graph", "master", "phases"])
+                    choices=["step", "grouped", "graph", "master", "phases", "noalloc"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-llama", action="store_true",
                     help="skip the extra llama-layer figures reported next to the owner share")
