@@ -22,6 +22,18 @@ __device__ __forceinline__ int owner_of(const int32_t* __restrict__ prefix, int 
     return lo;
 }
 
+// Shard slice of flattened element e of a sharded matrix (0 <= e < numel <=
+// 2^34, slices of slice >= 8 elements): e / slice without a 64-bit integer
+// division.  inv_slice = 1.0 / slice.  The double estimate e * inv_slice lies
+// within q 2^-51 of the quotient q < 2^31, well inside the 1 / slice distance
+// from q up to the next integer, so it truncates to floor(q) or, where q is an
+// integer, possibly to q - 1; one integer comparison makes it exact.
+__device__ __forceinline__ int64_t slice_index(int64_t e, int64_t slice, double inv_slice) {
+    int64_t k = int(double(e) * inv_slice);
+    k += (k + 1) * slice <= e ? 1 : 0;
+    return k;
+}
+
 // float32 -> bfloat16 bits, round to nearest even (IEEE-754 definition on the
 // bit pattern); NaN becomes a quiet NaN keeping sign and top payload bits.
 __device__ __forceinline__ uint16_t bf16_rne(float x) {

@@ -145,6 +145,7 @@ __global__ __launch_bounds__(kApplyThreads) void apply_kernel(
     const int64_t numel = mt.numel, off = o_compact ? mt.u_off : mt.off, poff = mt.poff;
     const int64_t slice = mt.slice_len, stride = mt.pstride;
     const bool sharded = slice != numel;
+    const double inv_slice = 1.0 / double(slice);
     const int64_t base = int64_t(blk - mt.chunk_begin) * kEwChunk;
 #pragma unroll
     for (int it = 0; it < kApplyIters; ++it) {
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(kApplyThreads) void apply_kernel(
             // slices are multiples of 8 long when sharded: a vector never straddles two
             int64_t dst = poff + j;
             if (sharded) {
-                const int64_t k = j / slice;
+                const int64_t k = slice_index(j, slice, inv_slice);
                 dst = poff + k * stride + (j - k * slice);
             }
             const float4 ov = load4_stream(o + off + j);
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(kApplyThreads) void apply_kernel(
             if (copy != nullptr) store_w(copy + dst, r);
         } else {
             for (int64_t k = j; k < numel && k < j + kEwVec; ++k) {
-                const int64_t s = sharded ? k / slice : 0;
+                const int64_t s = sharded ? slice_index(k, slice, inv_slice) : 0;
                 const int64_t dst = poff + s * stride + (k - s * slice);
                 const float w1 = load_w1(w + dst) * decay;
                 const float t = lr * o[off + k];

@@ -146,9 +146,9 @@ __global__ __launch_bounds__(256) void front_cast_kernel(const MatInfo* __restri
     const float beta = hv.beta;
     const int nesterov = hv.nesterov;
     // Each thread first loads all of its G and M (or U) groups and only then
-    // stores: vector memory counters complete in issue order and count stores,
-    // so a load issued after a store could not be waited for without waiting
-    // for the store.
+    // stores: loads and stores share the vector memory counter, and with both
+    // kinds pending a wait for a load is a wait for the counter to reach zero
+    // (their completion order is not known), store included.
     // G and M (or U, in gv) at 4 consecutive elements of U's row gr from column
     // gc; zero outside R x C.
     auto load4 = [&](int gr, int gc, float gv[4], float mv[4]) {

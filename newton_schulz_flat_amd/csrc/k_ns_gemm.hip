@@ -255,7 +255,7 @@ __device__ __forceinline__ void apply_span(TW* __restrict__ params, uint16_t* co
 // apply_span.  kU (O rows not a multiple of 4 long, unsharded matrix): every
 // complete group is loaded and stored element by element, its loads still
 // issued with the band's -- apply_span would wait for a store round trip per
-// element, since a load issued after a store completes only after it.
+// element, since a load issued after a store is waited for together with it.
 template <int kT, int kParts, bool kU, typename TW>
 __device__ __forceinline__ void apply_band(TW* __restrict__ params, uint16_t* copy, const MatInfo& mt,
                                            const float* wl, int pitch, int cpr, int a0, int b0,
