@@ -1,7 +1,7 @@
-"""The shard-slice index of the fused and standalone apply kernels (host check
+"""The shard-slice index of the standalone apply kernel (host check
 of its arithmetic, CPU only).
 
-For a sharded matrix the kernels find the slice of flattened element e as
+For a sharded matrix the kernel finds the slice of flattened element e as
 k = int(e * (1.0 / slice)) followed by one correction, k += ((k + 1) * slice
 <= e), instead of a 64-bit integer division.  IEEE-754 double multiplication
 and division are correctly rounded on the host as on the device, so this
