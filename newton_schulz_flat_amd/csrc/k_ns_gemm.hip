@@ -634,6 +634,13 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, const GemmTile 
             unsigned char* wbuf = q == 3 ? buf : nbuf;
             const int64_t kk = q == 3 ? k3 : k2, qkk = q == 3 ? qk3 : qk2;
             const int l0 = ((q + 1) & 3) * kPerStep;  // first pair of this step
+            // Step 3 (after the barrier) runs at raised wave priority, so that a
+            // wave already in the next block's step 0 yields issue slots to its
+            // partner on the SIMD still in step 3 (measured: llama layer about
+            // 1% faster, owner share unchanged).
+            if constexpr (BF16 && TILE == 256) {
+                if (q == 3) __builtin_amdgcn_s_setprio(1);
+            }
 #pragma unroll
             for (int m = 0; m < kMfma; ++m) {
                 const int i = m / kNj, j = m % kNj;
@@ -702,6 +709,9 @@ __device__ __forceinline__ void ns_gemm_tile(const NsArgs& args, const GemmTile 
 #pragma unroll
                 for (int l = 0; l < kL; ++l)
                     pb[l] = *reinterpret_cast<const u32x4*>(gq + l * qstep + qk3);
+            }
+            if constexpr (BF16 && TILE == 256) {
+                if (q == 3) __builtin_amdgcn_s_setprio(0);
             }
             if (q == 2) __syncthreads();
         }
